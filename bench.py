@@ -1,0 +1,232 @@
+"""Benchmark of the Lighthouse Attention layer on one MI355X.
+
+One step = lh_layer_fwd + lh_layer_bwd over one batch of synthetic input: the
+whole hot path (pyramid + scores, stratified top-K, gather, subsequence
+attention, scatter; scatter adjoint, attention backward, gather and pooling
+adjoints).  Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line.  Besides the headline (tokens/s of fwd+bwd), it reports
+per-stage times with algorithmic GB/s or TFLOP/s (stage mode: every stage
+entry point timed alone with HIP events on the stream its kernels run on),
+a roofline object for the dominant kernel, and the CPU oracle timed on a
+bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 4]
+                       [--no-cpu] [--no-stages]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=10)
+    return ap.parse_args()
+
+
+def algorithmic_work(w, S, E):
+    """Per layer call, all heads: bytes (memory-bound stages) or flops
+    (attention kernels), from the stage definitions.  e = element size."""
+    BH, N, d = w.B * w.H, w.N, w.d
+    e = 2 if w.dtype == "bf16" else 4
+    causal = S * (S + 1) / 2
+    return {
+        "pyramid_score": BH * (3 * N * d * e + 3 * (E - N) * d * e + 8 * E),
+        "topk_select": BH * (8 * E + 9 * S + 4 * E),
+        "gather": BH * (6 * S * d * e + 4 * S),
+        "attn_fwd_mfma": BH * 4 * d * causal,
+        "scatter": BH * (N * d * e + S * d * 4 + 9 * S),
+        "scatter_bwd": BH * (N * d * e + S * d * 4 + 9 * S),
+        "attn_bwd_dkv_mfma": BH * 8 * d * causal,
+        "attn_bwd_dq_mfma": BH * 2 * d * causal,
+        "gather_bwd": BH * (3 * N * d * e + 12 * S * d + 4 * E),
+    }
+
+
+FLOP_STAGES = {"attn_fwd_mfma", "attn_bwd_dkv_mfma", "attn_bwd_dq_mfma"}
+# stage -> the kernel it launches (for the roofline's rocprofv3 cross-check)
+KERNEL_OF = {
+    "attn_fwd_mfma": "attn_fwd_bf16_kernel",
+    "attn_bwd_dkv_mfma": "attn_bwd_dkv_kernel",
+    "attn_bwd_dq_mfma": "attn_bwd_dq_kernel",
+}
+
+
+def counters_for(kernel: str, workload_name: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except Exception:
+        return None
+    if not rec or rec.get("workload") != workload_name:
+        return None
+    src = os.path.join(ROOT, "sparse_long_context_amd", "csrc", rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sha256"]:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, Q, K, V, dO):
+    """The oracle as it stands, on head 0 of the workload: forward and
+    backward of one head, timed on this host; scaled to all heads."""
+    import threadpoolctl
+    from oracle import lighthouse as orc
+
+    g = orc.Geometry(w.N, w.p, w.L, w.K).check()
+    q, k, v, do = (x[0, 0].double().numpy() for x in (Q, K, V, dO))
+    t0 = time.perf_counter()
+    fw = orc.head_forward(q, k, v, g, store="bf16" if w.dtype == "bf16" else None)
+    orc.head_backward(fw, do)
+    dt = time.perf_counter() - t0
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    return {"value": w.N / (dt * w.H), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"head 0 of {w.H}, forward+backward of one head in {dt:.2f} s "
+                      f"(NumPy float64), rate scaled to all {w.H} heads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_long_context_amd import ops, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    Qc, Kc, Vc, dOc = synth.make_inputs(w)
+    io = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = io
+    Q, K, V = (x.to(dev) for x in (Qc, Kc, Vc))
+    dO = dOc.to(dev, out)
+    c = ops.Ctx(ops.make_dims(Q, w.p, w.L, w.S, out_dtype=out))
+    S, E = c.S, c.E
+
+    saved = ops.alloc_saved(c, dev)
+    o = torch.empty_like(Q, dtype=out)
+    ws = torch.empty(max(1, c.z.ws_layer_bwd), dtype=torch.uint8, device=dev)
+    grads = [torch.empty_like(Q, dtype=out) for _ in range(3)]
+
+    def step():
+        ops.layer_fwd(c, Q, K, V, saved=saved, o=o)
+        ops.layer_bwd(c, saved, dO, ws=ws, outs=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = w.B * w.N / (ms / 1e3)
+    print(f"[bench] layer fwd+bwd {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    stages, roof = None, None
+    if not args.no_stages and w.dtype == "bf16":
+        stages = {}
+        work = algorithmic_work(w, S, E)
+        r = {}
+        st = torch.cuda.current_stream()
+
+        def timed(name, fn):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            for _ in range(args.stage_reps):
+                res = fn()
+            b.record(st)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / args.stage_reps
+            wk = work.get(name)
+            ent = {"ms": round(t, 4)}
+            if wk is not None:
+                if name in FLOP_STAGES:
+                    ach = wk / (t / 1e3) / 1e12
+                    ent.update({"tflops": round(ach, 1), "frac_bf16_peak": round(ach / BF16_PEAK_TFLOPS, 4)})
+                else:
+                    ach = wk / (t / 1e3) / 1e9
+                    ent.update({"gbs": round(ach, 1), "frac_hbm_peak": round(ach / HBM_PEAK_GBS, 4)})
+            stages[name] = ent
+            return res
+
+        r["pq"], r["pk"], r["pv"], r["sq"], r["sk"] = timed("pyramid_score", lambda: ops.pyramid_score(c, Q, K, V))
+        r["idx"], r["anc"], r["fl"], r["row_of"] = timed("topk_select", lambda: ops.topk_select(c, r["sq"], r["sk"]))
+        r["qs"], r["ks"], r["vs"], r["qst"], r["kst"], r["vst"] = timed(
+            "gather", lambda: ops.gather(c, Q, K, V, r["pq"], r["pk"], r["pv"], r["idx"], transposed=True))
+        os_ = torch.empty(w.B, w.H, S, w.d, dtype=torch.float32, device=dev)
+        lse = torch.empty(w.B, w.H, S, dtype=torch.float32, device=dev)
+        timed("attn_fwd_mfma", lambda: ops.attn_fwd_mfma(c, r["qs"], r["ks"], r["vst"], r["fl"], os_, lse))
+        timed("scatter", lambda: ops.scatter(c, os_, r["anc"], r["fl"]))
+        dos = timed("scatter_bwd", lambda: ops.scatter_bwd(c, dO, r["anc"], r["fl"]))
+        hi, lo, thi, tlo, drow = timed("attn_bwd_prep", lambda: ops.attn_bwd_prep(c, dos, os_))
+        dks = torch.empty(w.B, w.H, S, w.d, dtype=torch.float32, device=dev)
+        dvs, dqs = torch.empty_like(dks), torch.empty_like(dks)
+        timed("attn_bwd_dkv_mfma", lambda: ops.attn_bwd_dkv_mfma(c, r["qs"], r["ks"], r["vs"], r["qst"], hi, lo,
+                                                                 thi, tlo, lse, drow, r["fl"], dks, dvs))
+        timed("attn_bwd_dq_mfma", lambda: ops.attn_bwd_dq_mfma(c, r["qs"], r["ks"], r["vs"], r["kst"], hi, lo,
+                                                               lse, drow, r["fl"], dqs))
+        timed("gather_bwd", lambda: ops.gather_bwd(c, dqs, dks, dvs, r["row_of"]))
+        # dominant kernel: the single-kernel stage with the largest time
+        name = max((n for n in stages if n in KERNEL_OF), key=lambda n: stages[n]["ms"])
+        t = stages[name]["ms"] / 1e3
+        ach = work[name] / t / 1e12
+        traffic = counters_for(KERNEL_OF[name], w.name)
+        roof = {"kernel": KERNEL_OF[name], "bound": "mfma", "achieved": round(ach, 2),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "avg_launch_ms": round(stages[name]["ms"], 4),
+                "algorithmic_per_launch": work[name]}
+        for n, e in stages.items():
+            print(f"[bench] stage {n:20s} {e}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, Qc, Kc, Vc, dOc.to(out))
+
+    line = {
+        "metric": "Lighthouse layer fwd+bwd tokens/sec at N=128K; per-stage HBM GB/s, MFMA util",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "N": w.N, "H": w.H, "d": w.d, "p": w.p,
+                   "L": w.L, "S": S, "K": w.K, "io_dtype": w.dtype, "out_dtype": w.dtype},
+        "roofline": roof, "cpu_baseline": cpu, "stages": stages,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

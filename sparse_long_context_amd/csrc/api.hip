@@ -1,0 +1,484 @@
+// Public C ABI of liblighthouse: validation, sizes, and the stage / layer
+// entry points declared in include/lighthouse.h.  Host code only; the
+// kernels live in the k_*.hip sources.
+#include <math.h>
+#include <string.h>
+
+#include "lh_internal.h"
+
+namespace lh {
+
+static bool mul_ok(int64_t a, int64_t b, int64_t lim, int64_t *out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > lim / a) return false;
+  *out = a * b;
+  return true;
+}
+
+lh_status make_geo(const lh_dims *dm, Geo *g) {
+  if (!dm || !g) return LH_ERR_INVALID_ARG;
+  memset(g, 0, sizeof(*g));
+  if (dm->B < 1 || dm->H < 1 || dm->N < 1 || dm->p < 2 || dm->L < 1 || dm->d < 1)
+    return LH_ERR_INVALID_ARG;
+  if (dm->reserved != 0) return LH_ERR_INVALID_ARG;
+  if (dm->L >= kMaxLevels) return LH_ERR_UNSUPPORTED;
+  if (!(dm->scale >= 0.0f) || !isfinite(dm->scale)) return LH_ERR_INVALID_ARG;
+  if ((dm->io_dtype != LH_F32 && dm->io_dtype != LH_BF16) ||
+      (dm->out_dtype != LH_F32 && dm->out_dtype != LH_BF16))
+    return LH_ERR_INVALID_ARG;
+  const int64_t lim = (int64_t)1 << 40;
+  g->B = dm->B; g->N = dm->N; g->H = dm->H; g->d = dm->d; g->p = dm->p; g->L = dm->L;
+  g->K = dm->K; g->S = dm->S; g->io = dm->io_dtype; g->out = dm->out_dtype;
+  g->pw[0] = 1;
+  for (int l = 1; l <= g->L; ++l)
+    if (!mul_ok(g->pw[l - 1], g->p, lim, &g->pw[l])) return LH_ERR_INVALID_ARG;
+  g->Bc = g->pw[g->L - 1];
+  if (g->Bc > g->N || g->N % g->Bc) return LH_ERR_INVALID_ARG;
+  g->n_c = g->N / g->Bc;
+  g->T = (g->pw[g->L] - 1) / (g->p - 1);
+  int64_t off = 0;
+  for (int l = 0; l < g->L; ++l) {
+    g->lsize[l] = g->N / g->pw[l];
+    g->loff[l] = off;
+    off += g->lsize[l];
+  }
+  g->E = off;
+  if (g->K < 0 || g->K % g->n_c) return LH_ERR_INVALID_ARG;
+  g->k_s = g->K / g->n_c;
+  if (g->k_s > g->T - 1) return LH_ERR_INVALID_ARG;
+  if (g->S != g->K + g->n_c) return LH_ERR_INVALID_ARG;
+  if (g->E >= ((int64_t)1 << 31) || g->S >= ((int64_t)1 << 31)) return LH_ERR_UNSUPPORTED;
+  if (g->BH() > 65535) return LH_ERR_UNSUPPORTED;
+  if (g->d != 64 && g->d != 128) return LH_ERR_UNSUPPORTED;
+  if (g->io == LH_F32 && g->out != LH_F32) return LH_ERR_UNSUPPORTED;
+  g->Sp = (g->S + 63) / 64 * 64;
+  g->scale = dm->scale == 0.0f ? (float)(1.0 / sqrt((double)g->d)) : dm->scale;
+  lh_status s = check_pyramid_supported(*g);
+  if (s != LH_OK) return s;
+  return check_select_supported(*g);
+}
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Sizes {
+  size_t subseq, subseq_t, rowf32, subseq_f32, drow;
+};
+
+static Sizes sizes_of(const Geo &g) {
+  Sizes z;
+  const size_t bh = (size_t)g.BH();
+  z.subseq = bh * g.S * g.d * el_size(g.io);
+  z.subseq_t = bh * g.d * g.Sp * 2;
+  z.subseq_f32 = bh * g.S * g.d * 4;
+  z.drow = bh * g.S * 4;
+  return z;
+}
+
+static size_t ws_attn_fwd(const Geo &g) {
+  return g.io == LH_BF16 ? al256(sizes_of(g).subseq_t) : 0;
+}
+static size_t rows_bf16(const Geo &g) { return (size_t)g.BH() * g.S * g.d * 2; }
+static size_t ws_attn_bwd(const Geo &g) {
+  Sizes z = sizes_of(g);
+  if (g.io == LH_F32) return al256(z.drow);
+  // dos split (hi, lo) rows and transposes, qs^T, ks^T, drow
+  return 2 * al256(rows_bf16(g)) + 4 * al256(z.subseq_t) + al256(z.drow);
+}
+static size_t ws_layer_bwd(const Geo &g) {
+  Sizes z = sizes_of(g);
+  size_t b = 3 * al256(z.subseq_f32) + al256(z.drow);   // dqs, dks, dvs, drow
+  if (g.io == LH_BF16) b += 2 * al256(rows_bf16(g)) + 2 * al256(z.subseq_t);
+  else b += al256(z.subseq_f32);                          // float32 dos
+  return b;
+}
+
+// carve consecutive 256-aligned sub-buffers out of a workspace
+struct Carver {
+  char *base;
+  size_t off, cap;
+  void *take(size_t n) {
+    void *p = base + off;
+    off += al256(n);
+    return p;
+  }
+  bool ok() const { return off <= cap; }
+};
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+static bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
+
+}  // namespace lh
+
+using namespace lh;
+
+#define LH_TRY(expr)                   \
+  do {                                 \
+    lh_status _s = (expr);             \
+    if (_s != LH_OK) return _s;        \
+  } while (0)
+#define LH_REQ(cond)                              \
+  do {                                            \
+    if (!(cond)) return LH_ERR_INVALID_ARG;       \
+  } while (0)
+
+extern "C" {
+
+lh_status lh_validate(const lh_dims *dims) {
+  Geo g;
+  return make_geo(dims, &g);
+}
+
+lh_status lh_get_sizes(const lh_dims *dims, lh_sizes *out) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(out);
+  memset(out, 0, sizeof(*out));
+  const size_t bh = (size_t)g.BH();
+  out->E = g.E; out->n_c = g.n_c; out->T = g.T; out->k_s = g.k_s; out->Bc = g.Bc; out->Sp = g.Sp;
+  out->pyramid_bytes = bh * (g.E - g.N) * g.d * el_size(g.io);
+  out->score_bytes = bh * g.E * 4;
+  out->row_i32_bytes = bh * g.S * 4;
+  out->row_u8_bytes = bh * g.S;
+  out->row_of_bytes = bh * g.E * 4;
+  out->subseq_bytes = g.io == LH_BF16 ? bh * g.d * g.Sp * 2 : bh * g.S * g.d * 4;
+  if (g.io == LH_BF16 && bh * g.S * g.d * 2 > out->subseq_bytes) out->subseq_bytes = bh * g.S * g.d * 2;
+  out->os_bytes = bh * g.S * g.d * 4;
+  out->lse_bytes = bh * g.S * 4;
+  out->token_io_bytes = bh * g.N * g.d * el_size(g.io);
+  out->token_out_bytes = bh * g.N * g.d * el_size(g.out);
+  out->ws_attn_fwd = ws_attn_fwd(g);
+  out->ws_attn_bwd = ws_attn_bwd(g);
+  out->ws_layer_fwd = 0;
+  out->ws_layer_bwd = ws_layer_bwd(g);
+  return LH_OK;
+}
+
+const char *lh_status_string(lh_status s) {
+  switch (s) {
+    case LH_OK: return "ok";
+    case LH_ERR_INVALID_ARG: return "invalid argument (geometry, null or misaligned pointer)";
+    case LH_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LH_ERR_WORKSPACE: return "workspace missing or too small";
+    case LH_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *lh_version(void) { return "0.1.0"; }
+
+lh_status lh_pyramid_build(const lh_dims *dims, const void *q, const void *k, const void *v,
+                           void *pq, void *pk, void *pv, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  const void *in[3] = {q, k, v};
+  void *out[3] = {pq, pk, pv};
+  int any = 0;
+  for (int i = 0; i < 3; ++i) {
+    LH_REQ(g.L == 1 || (in[i] == nullptr) == (out[i] == nullptr));
+    LH_REQ(aligned16(in[i]) && aligned16(out[i]));
+    any += in[i] != nullptr;
+  }
+  LH_REQ(any > 0);
+  return launch_pyramid_score(g, q, k, v, pq, pk, pv, nullptr, nullptr, (hipStream_t)stream);
+}
+
+lh_status lh_score(const lh_dims *dims, const void *q, const void *k, float *sq, float *sk,
+                   lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(q && k && sq && sk && aligned16(q) && aligned16(k) && aligned4(sq) && aligned4(sk));
+  return launch_pyramid_score(g, q, k, nullptr, nullptr, nullptr, nullptr, sq, sk,
+                              (hipStream_t)stream);
+}
+
+lh_status lh_pyramid_score(const lh_dims *dims, const void *q, const void *k, const void *v,
+                           void *pq, void *pk, void *pv, float *sq, float *sk,
+                           lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(q && k && v && sq && sk);
+  LH_REQ(g.L == 1 || (pq && pk && pv));
+  LH_REQ(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(pq) && aligned16(pk) &&
+         aligned16(pv) && aligned4(sq) && aligned4(sk));
+  return launch_pyramid_score(g, q, k, v, pq, pk, pv, sq, sk, (hipStream_t)stream);
+}
+
+lh_status lh_topk_select(const lh_dims *dims, const float *sq, const float *sk,
+                         int32_t *sel_idx, int32_t *sel_anchor, uint8_t *sel_flags,
+                         int32_t *row_of, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(sq && sk && sel_idx && sel_anchor && sel_flags && row_of);
+  LH_REQ(aligned4(sq) && aligned4(sk) && aligned4(sel_idx) && aligned4(sel_anchor) &&
+         aligned4(row_of));
+  return launch_select(g, sq, sk, sel_idx, sel_anchor, sel_flags, row_of, (hipStream_t)stream);
+}
+
+static lh_status gather_impl(const Geo &g, const void *q, const void *k, const void *v,
+                             const void *pq, const void *pk, const void *pv,
+                             const int32_t *sel_idx, void *qs, void *ks, void *vs, void *qst,
+                             void *kst, void *vst, hipStream_t st) {
+  const void *src[3] = {q, k, v};
+  const void *psrc[3] = {pq, pk, pv};
+  void *dst[3] = {qs, ks, vs};
+  LH_TRY(launch_gather(g, src, psrc, sel_idx, dst, st));
+  void *tr[3] = {qst, kst, vst};
+  for (int i = 0; i < 3; ++i)
+    if (tr[i]) LH_TRY(launch_transpose(g, dst[i], tr[i], st));
+  return LH_OK;
+}
+
+lh_status lh_gather(const lh_dims *dims, const void *q, const void *k, const void *v,
+                    const void *pq, const void *pk, const void *pv, const int32_t *sel_idx,
+                    void *qs, void *ks, void *vs, void *qst, void *kst, void *vst,
+                    lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(q && k && v && sel_idx && qs && ks && vs);
+  LH_REQ(g.L == 1 || (pq && pk && pv));
+  LH_REQ(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(pq) && aligned16(pk) &&
+         aligned16(pv) && aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned4(sel_idx));
+  LH_REQ(aligned16(qst) && aligned16(kst) && aligned16(vst));
+  if (g.io == LH_F32) LH_REQ(!qst && !kst && !vst);
+  return gather_impl(g, q, k, v, pq, pk, pv, sel_idx, qs, ks, vs, qst, kst, vst,
+                     (hipStream_t)stream);
+}
+
+lh_status lh_subseq_attn_fwd(const lh_dims *dims, const void *qs, const void *ks,
+                             const void *vs, const uint8_t *sel_flags, void *os, float *lse,
+                             void *ws, size_t ws_bytes, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(qs && ks && vs && sel_flags && os && lse);
+  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(os) && aligned4(lse));
+  hipStream_t st = (hipStream_t)stream;
+  if (g.io == LH_F32)
+    return launch_attn_fwd_f32(g, (const float *)qs, (const float *)ks, (const float *)vs,
+                               sel_flags, (float *)os, lse, st);
+  const size_t need = ws_attn_fwd(g);
+  if (ws_bytes < need || !ws || !aligned16(ws)) return LH_ERR_WORKSPACE;
+  LH_TRY(launch_transpose(g, vs, ws, st));
+  return launch_attn_fwd_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)ws,
+                              sel_flags, (float *)os, lse, st);
+}
+
+lh_status lh_subseq_attn_bwd(const lh_dims *dims, const void *qs, const void *ks,
+                             const void *vs, const void *os, const float *lse,
+                             const uint8_t *sel_flags, const float *dos, float *dqs, float *dks,
+                             float *dvs, void *ws, size_t ws_bytes, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(qs && ks && vs && os && lse && sel_flags && dos && dqs && dks && dvs);
+  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(os) && aligned4(lse) &&
+         aligned16(dos) && aligned16(dqs) && aligned16(dks) && aligned16(dvs));
+  const size_t need = ws_attn_bwd(g);
+  if (ws_bytes < need || !ws || !aligned16(ws)) return LH_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c{(char *)ws, 0, ws_bytes};
+  Sizes z = sizes_of(g);
+  if (g.io == LH_F32) {
+    float *drow = (float *)c.take(z.drow);
+    LH_TRY(launch_dos_prep(g, dos, (const float *)os, nullptr, nullptr, drow, st));
+    return launch_attn_bwd_f32(g, (const float *)qs, (const float *)ks, (const float *)vs,
+                               (const float *)os, lse, sel_flags, dos, drow, dqs, dks, dvs, st);
+  }
+  bf16_t *dhi = (bf16_t *)c.take(rows_bf16(g));
+  bf16_t *dlo = (bf16_t *)c.take(rows_bf16(g));
+  bf16_t *dthi = (bf16_t *)c.take(z.subseq_t);
+  bf16_t *dtlo = (bf16_t *)c.take(z.subseq_t);
+  bf16_t *qst = (bf16_t *)c.take(z.subseq_t);
+  bf16_t *kst = (bf16_t *)c.take(z.subseq_t);
+  float *drow = (float *)c.take(z.drow);
+  if (!c.ok()) return LH_ERR_WORKSPACE;
+  LH_TRY(launch_dos_prep(g, dos, (const float *)os, dhi, dlo, drow, st));
+  LH_TRY(launch_transpose(g, dhi, dthi, st));
+  LH_TRY(launch_transpose(g, dlo, dtlo, st));
+  LH_TRY(launch_transpose(g, qs, qst, st));
+  LH_TRY(launch_transpose(g, ks, kst, st));
+  return launch_attn_bwd_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
+                              qst, kst, dhi, dlo, dthi, dtlo, lse, drow, sel_flags, dqs, dks,
+                              dvs, st);
+}
+
+lh_status lh_attn_bwd_prep(const lh_dims *dims, const float *dos, const float *os, void *dos_hi,
+                           void *dos_lo, void *dost_hi, void *dost_lo, float *drow,
+                           lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  if (g.io != LH_BF16) return LH_ERR_UNSUPPORTED;
+  LH_REQ(dos && os && dos_hi && dos_lo && dost_hi && dost_lo && drow);
+  LH_REQ(aligned16(dos) && aligned16(os) && aligned16(dos_hi) && aligned16(dos_lo) &&
+         aligned16(dost_hi) && aligned16(dost_lo) && aligned4(drow));
+  hipStream_t st = (hipStream_t)stream;
+  LH_TRY(launch_dos_prep(g, dos, os, (bf16_t *)dos_hi, (bf16_t *)dos_lo, drow, st));
+  LH_TRY(launch_transpose(g, dos_hi, dost_hi, st));
+  return launch_transpose(g, dos_lo, dost_lo, st);
+}
+
+lh_status lh_attn_fwd_mfma(const lh_dims *dims, const void *qs, const void *ks, const void *vst,
+                           const uint8_t *sel_flags, float *os, float *lse, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  if (g.io != LH_BF16) return LH_ERR_UNSUPPORTED;
+  LH_REQ(qs && ks && vst && sel_flags && os && lse);
+  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vst) && aligned16(os) && aligned4(lse));
+  return launch_attn_fwd_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vst,
+                              sel_flags, os, lse, (hipStream_t)stream);
+}
+
+lh_status lh_attn_bwd_dkv_mfma(const lh_dims *dims, const void *qs, const void *ks,
+                               const void *vs, const void *qst, const void *dos_hi,
+                               const void *dos_lo, const void *dost_hi, const void *dost_lo,
+                               const float *lse, const float *drow, const uint8_t *sel_flags,
+                               float *dks, float *dvs, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  if (g.io != LH_BF16) return LH_ERR_UNSUPPORTED;
+  LH_REQ(qs && ks && vs && qst && dos_hi && dos_lo && dost_hi && dost_lo && lse && drow &&
+         sel_flags && dks && dvs);
+  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(qst) &&
+         aligned16(dos_hi) && aligned16(dos_lo) && aligned16(dost_hi) && aligned16(dost_lo) &&
+         aligned4(lse) && aligned4(drow) && aligned16(dks) && aligned16(dvs));
+  return launch_attn_bwd_dkv_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
+                                  (const bf16_t *)qst, (const bf16_t *)dos_hi,
+                                  (const bf16_t *)dos_lo, (const bf16_t *)dost_hi,
+                                  (const bf16_t *)dost_lo, lse, drow, sel_flags, dks, dvs,
+                                  (hipStream_t)stream);
+}
+
+lh_status lh_attn_bwd_dq_mfma(const lh_dims *dims, const void *qs, const void *ks,
+                              const void *vs, const void *kst, const void *dos_hi,
+                              const void *dos_lo, const float *lse, const float *drow,
+                              const uint8_t *sel_flags, float *dqs, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  if (g.io != LH_BF16) return LH_ERR_UNSUPPORTED;
+  LH_REQ(qs && ks && vs && kst && dos_hi && dos_lo && lse && drow && sel_flags && dqs);
+  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(kst) &&
+         aligned16(dos_hi) && aligned16(dos_lo) && aligned4(lse) && aligned4(drow) &&
+         aligned16(dqs));
+  return launch_attn_bwd_dq_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
+                                 (const bf16_t *)kst, (const bf16_t *)dos_hi,
+                                 (const bf16_t *)dos_lo, lse, drow, sel_flags, dqs,
+                                 (hipStream_t)stream);
+}
+
+lh_status lh_scatter(const lh_dims *dims, const void *os, const int32_t *sel_anchor,
+                     const uint8_t *sel_flags, void *o, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(os && sel_anchor && sel_flags && o);
+  LH_REQ(aligned16(os) && aligned16(o) && aligned4(sel_anchor));
+  return launch_scatter(g, (const float *)os, sel_anchor, sel_flags, o, (hipStream_t)stream);
+}
+
+lh_status lh_scatter_bwd(const lh_dims *dims, const void *dout, const int32_t *sel_anchor,
+                         const uint8_t *sel_flags, float *dos, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(dout && sel_anchor && sel_flags && dos);
+  LH_REQ(aligned16(dout) && aligned16(dos) && aligned4(sel_anchor));
+  return launch_scatter_bwd(g, dout, sel_anchor, sel_flags, dos, nullptr, nullptr, nullptr,
+                            nullptr, (hipStream_t)stream);
+}
+
+lh_status lh_gather_bwd(const lh_dims *dims, const float *dqs, const float *dks,
+                        const float *dvs, const int32_t *row_of, void *dq, void *dk, void *dv,
+                        lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(dqs && dks && dvs && row_of && dq && dk && dv);
+  LH_REQ(aligned16(dqs) && aligned16(dks) && aligned16(dvs) && aligned4(row_of) &&
+         aligned16(dq) && aligned16(dk) && aligned16(dv));
+  const float *in[3] = {dqs, dks, dvs};
+  void *out[3] = {dq, dk, dv};
+  return launch_unpool(g, in, row_of, out, (hipStream_t)stream);
+}
+
+static lh_status check_saved(const Geo &g, const lh_saved *s) {
+  LH_REQ(s);
+  LH_REQ(s->sq && s->sk && s->sel_idx && s->sel_anchor && s->sel_flags && s->row_of);
+  LH_REQ(s->qs && s->ks && s->vs && s->os && s->lse);
+  LH_REQ(g.L == 1 || (s->pq && s->pk && s->pv));
+  LH_REQ(aligned16(s->pq) && aligned16(s->pk) && aligned16(s->pv) && aligned4(s->sq) &&
+         aligned4(s->sk) && aligned4(s->sel_idx) && aligned4(s->sel_anchor) &&
+         aligned4(s->row_of) && aligned16(s->qs) && aligned16(s->ks) && aligned16(s->vs) &&
+         aligned16(s->os) && aligned4(s->lse));
+  if (g.io == LH_BF16) {
+    LH_REQ(s->qst && s->kst && s->vst);
+    LH_REQ(aligned16(s->qst) && aligned16(s->kst) && aligned16(s->vst));
+  }
+  return LH_OK;
+}
+
+lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const void *v,
+                       void *o, const lh_saved *s, void *ws, size_t ws_bytes,
+                       lh_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(q && k && v && o);
+  LH_REQ(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o));
+  LH_TRY(check_saved(g, s));
+  hipStream_t st = (hipStream_t)stream;
+  LH_TRY(launch_pyramid_score(g, q, k, v, s->pq, s->pk, s->pv, s->sq, s->sk, st));
+  LH_TRY(launch_select(g, s->sq, s->sk, s->sel_idx, s->sel_anchor, s->sel_flags, s->row_of, st));
+  const bool bf = g.io == LH_BF16;
+  LH_TRY(gather_impl(g, q, k, v, s->pq, s->pk, s->pv, s->sel_idx, s->qs, s->ks, s->vs,
+                     bf ? s->qst : nullptr, bf ? s->kst : nullptr, bf ? s->vst : nullptr, st));
+  if (bf)
+    LH_TRY(launch_attn_fwd_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
+                                (const bf16_t *)s->vst, s->sel_flags, (float *)s->os, s->lse,
+                                st));
+  else
+    LH_TRY(launch_attn_fwd_f32(g, (const float *)s->qs, (const float *)s->ks,
+                               (const float *)s->vs, s->sel_flags, (float *)s->os, s->lse, st));
+  return launch_scatter(g, (const float *)s->os, s->sel_anchor, s->sel_flags, o, st);
+}
+
+lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout, void *dq,
+                       void *dk, void *dv, void *ws, size_t ws_bytes, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(dout && dq && dk && dv);
+  LH_REQ(aligned16(dout) && aligned16(dq) && aligned16(dk) && aligned16(dv));
+  LH_TRY(check_saved(g, s));
+  const size_t need = ws_layer_bwd(g);
+  if (ws_bytes < need || !ws || !aligned16(ws)) return LH_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  Sizes z = sizes_of(g);
+  Carver c{(char *)ws, 0, ws_bytes};
+  float *dqs = (float *)c.take(z.subseq_f32);
+  float *dks = (float *)c.take(z.subseq_f32);
+  float *dvs = (float *)c.take(z.subseq_f32);
+  float *drow = (float *)c.take(z.drow);
+  if (g.io == LH_BF16) {
+    bf16_t *dhi = (bf16_t *)c.take(rows_bf16(g));
+    bf16_t *dlo = (bf16_t *)c.take(rows_bf16(g));
+    bf16_t *dthi = (bf16_t *)c.take(z.subseq_t);
+    bf16_t *dtlo = (bf16_t *)c.take(z.subseq_t);
+    if (!c.ok()) return LH_ERR_WORKSPACE;
+    LH_TRY(launch_scatter_bwd(g, dout, s->sel_anchor, s->sel_flags, nullptr, dhi, dlo, (const float *)s->os,
+                              drow, st));
+    LH_TRY(launch_transpose(g, dhi, dthi, st));
+    LH_TRY(launch_transpose(g, dlo, dtlo, st));
+    LH_TRY(launch_attn_bwd_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
+                                (const bf16_t *)s->vs, (const bf16_t *)s->qst,
+                                (const bf16_t *)s->kst, dhi, dlo, dthi, dtlo, s->lse, drow,
+                                s->sel_flags, dqs, dks, dvs, st));
+  } else {
+    float *dos = (float *)c.take(z.subseq_f32);
+    if (!c.ok()) return LH_ERR_WORKSPACE;
+    LH_TRY(launch_scatter_bwd(g, dout, s->sel_anchor, s->sel_flags, dos, nullptr, nullptr, (const float *)s->os,
+                              drow, st));
+    LH_TRY(launch_attn_bwd_f32(g, (const float *)s->qs, (const float *)s->ks,
+                               (const float *)s->vs, (const float *)s->os, s->lse, s->sel_flags,
+                               dos, drow, dqs, dks, dvs, st));
+  }
+  const float *in[3] = {dqs, dks, dvs};
+  void *out[3] = {dq, dk, dv};
+  return launch_unpool(g, in, s->row_of, out, st);
+}
+
+}  // extern "C"

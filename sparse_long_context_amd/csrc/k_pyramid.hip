@@ -1,0 +1,225 @@
+// Stage 1 + 2a: symmetric average-pooled pyramid and l2 scores with max-pool
+// inheritance, in one pass over Q, K, V.
+//
+// Method (gist.science explainer "Long Context Pre-Training with Lighthouse
+// Attention", technical summary 2.A and 2.B; edge.aivizor.me news item,
+// four-stages paragraph): level l entry i is the mean of p consecutive
+// level-(l-1) entries, for Q, K and V alike; every entry carries two scores,
+// the l2 norms of its level-0 q and k rows, and coarse entries take the max
+// of their children.
+//
+// Work decomposition.  One workgroup covers `spw` whole coarsest cells
+// (strata) of one (b, h) and one tensor.  A thread owns an 8-column slice
+// (CPR = d/8 threads per row) of one level-g subtree (G = p^g consecutive
+// tokens) and streams its tokens once, keeping the running sums of levels
+// 1..g in registers (a carry chain: when a level-l entry completes, its sum
+// moves into level l+1).  The level-g sums of the workgroup's subtrees go to
+// LDS, where levels g+1..L-1 of each stratum are formed.  Every input byte is
+// read once and every output byte written once; the kernel is HBM-bound.
+//
+// Rounding: sums are float32; each pyramid entry is rounded once from its
+// float32 sum (sum / p^l) to the I/O type.  Squares of a row are summed in
+// float64 and the square root is rounded once to float32.
+#include "lh_internal.h"
+
+namespace lh {
+
+constexpr int kPyrMaxG = 6;       // deepest per-thread carry chain
+constexpr int kPyrThreads = 256;  // workgroup size cap
+
+struct PyrArgs {
+  const void *in[3];
+  void *pyr[3];
+  float *score[3];   // sq for tensor 0, sk for tensor 1, none for V
+  int64_t N, E, Bc;
+  int32_t d, p, L, g, R, spw;
+  int64_t lsize[kMaxLevels], loff[kMaxLevels], pw[kMaxLevels + 1];
+};
+
+template <typename T, int CPR>
+__global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
+  extern __shared__ float lds[];                 // [spw*R][d] sums, then [spw*R] maxima
+  const int z = blockIdx.z;
+  const T *X = (const T *)a.in[z];
+  if (!X) return;
+  const int64_t bh = blockIdx.y;
+  const int d = a.d;
+  X += bh * a.N * d;
+  T *P = a.pyr[z] ? (T *)a.pyr[z] + bh * (a.E - a.N) * d : nullptr;
+  float *Sc = a.score[z] ? a.score[z] + bh * a.E : nullptr;
+  const bool do_pyr = P != nullptr, do_sc = Sc != nullptr;
+
+  const int tid = threadIdx.x;
+  const int c = tid % CPR;                 // column slice
+  const int rs = tid / CPR;                // row slot in workgroup
+  const int sub = rs / a.R, r = rs % a.R;  // stratum within workgroup, subtree
+  const int64_t m = (int64_t)blockIdx.x * a.spw + sub;
+  const int G = (int)a.pw[a.g];
+  const int64_t base = m * a.Bc + (int64_t)r * G;
+  const int rows = a.spw * a.R;
+  float *lsum = lds;                       // [rows][d]
+  float *lmax = lds + (size_t)rows * d;    // [rows]
+
+  float acc[kPyrMaxG + 2][8];
+  float smx[kPyrMaxG + 2];
+#pragma unroll
+  for (int l = 0; l <= kPyrMaxG + 1; ++l) {
+    smx[l] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[l][i] = 0.f;
+  }
+
+  for (int t0 = 0; t0 < G; t0 += 4) {
+    float x[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (t0 + u < G) load8(X + (base + t0 + u) * d + c * 8, x[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (t0 + u >= G) break;
+      const int64_t tok = base + t0 + u;
+      float s = 0.f;
+      if (do_sc) {
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += (double)x[u][i] * (double)x[u][i];
+#pragma unroll
+        for (int off = CPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+        s = (float)sqrt(ss);
+        if (c == 0) Sc[tok] = s;
+      }
+      if (a.g == 0) {
+        // the subtree is a single token: it goes straight to LDS
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lsum[(size_t)rs * d + c * 8 + i] = x[u][i];
+        if (c == 0) lmax[rs] = s;
+        continue;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[1][i] += x[u][i];
+      smx[1] = fmaxf(smx[1], s);
+      const int64_t cnt = t0 + u + 1;
+#pragma unroll
+      for (int l = 1; l <= kPyrMaxG; ++l) {
+        if (l > a.g || cnt % a.pw[l] != 0) break;
+        const int64_t idx = (tok + 1) / a.pw[l] - 1;   // index within level l
+        if (do_pyr) {
+          const float inv = (float)a.pw[l];
+          float mean[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mean[i] = acc[l][i] / inv;
+          store8(P + (a.loff[l] - a.N + idx) * d + c * 8, mean);
+        }
+        if (do_sc && c == 0) Sc[a.loff[l] + idx] = smx[l];
+        if (l == a.g) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) lsum[(size_t)rs * d + c * 8 + i] = acc[l][i];
+          if (c == 0) lmax[rs] = smx[l];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[l + 1][i] += acc[l][i];
+          smx[l + 1] = fmaxf(smx[l + 1], smx[l]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[l][i] = 0.f;
+        smx[l] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // levels g+1 .. L-1 of each stratum from the LDS sums (compacted in place:
+  // entry e of the current level lives in row sub*R + e)
+  int n = a.R;
+  for (int l = a.g + 1; l < a.L; ++l) {
+    n /= a.p;
+    const bool act = rs < a.spw * n;
+    const int s2 = act ? rs / n : 0, e = act ? rs % n : 0;
+    float sum[8];
+    float mx = 0.f;
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum[i] = 0.f;
+      for (int k = 0; k < a.p; ++k) {
+        const int row = s2 * a.R + e * a.p + k;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sum[i] += lsum[(size_t)row * d + c * 8 + i];
+        mx = fmaxf(mx, lmax[row]);
+      }
+    }
+    __syncthreads();
+    if (act) {
+      const int row = s2 * a.R + e;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lsum[(size_t)row * d + c * 8 + i] = sum[i];
+      if (c == 0) lmax[row] = mx;
+      const int64_t mm = (int64_t)blockIdx.x * a.spw + s2;
+      const int64_t idx = mm * n + e;
+      if (do_pyr) {
+        const float inv = (float)a.pw[l];
+        float mean[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mean[i] = sum[i] / inv;
+        store8(P + (a.loff[l] - a.N + idx) * d + c * 8, mean);
+      }
+      if (do_sc && c == 0) Sc[a.loff[l] + idx] = mx;
+    }
+    __syncthreads();
+  }
+}
+
+// chain depth g, subtrees per stratum R, strata per workgroup spw
+static bool pyr_plan(const Geo &g, int *gd, int *R, int *spw) {
+  const int cpr = g.d / 8;
+  for (int gg = 0; gg <= kPyrMaxG && gg < g.L; ++gg) {
+    const int64_t r = g.Bc / g.pw[gg];
+    if (r * cpr <= kPyrThreads) {
+      int s = (int)(kPyrThreads / (r * cpr));
+      while (s > 1 && g.n_c % s) --s;
+      *gd = gg;
+      *R = (int)r;
+      *spw = s;
+      return true;
+    }
+  }
+  return false;
+}
+
+lh_status check_pyramid_supported(const Geo &g) {
+  int a, b, c;
+  return pyr_plan(g, &a, &b, &c) ? LH_OK : LH_ERR_UNSUPPORTED;
+}
+
+lh_status launch_pyramid_score(const Geo &g, const void *q, const void *k, const void *v,
+                               void *pq, void *pk, void *pv, float *sq, float *sk,
+                               hipStream_t st) {
+  PyrArgs a;
+  a.in[0] = q; a.in[1] = k; a.in[2] = v;
+  a.pyr[0] = pq; a.pyr[1] = pk; a.pyr[2] = pv;
+  if (g.L == 1) a.pyr[0] = a.pyr[1] = a.pyr[2] = nullptr;   // no coarse levels
+  a.score[0] = sq; a.score[1] = sk; a.score[2] = nullptr;
+  // a tensor with neither pyramid nor score output is skipped
+  for (int z = 0; z < 3; ++z)
+    if (!a.pyr[z] && !a.score[z]) a.in[z] = nullptr;
+  a.N = g.N; a.E = g.E; a.Bc = g.Bc; a.d = g.d; a.p = g.p; a.L = g.L;
+  for (int l = 0; l < kMaxLevels; ++l) { a.lsize[l] = g.lsize[l]; a.loff[l] = g.loff[l]; }
+  for (int l = 0; l <= kMaxLevels; ++l) a.pw[l] = g.pw[l];
+  if (!pyr_plan(g, &a.g, &a.R, &a.spw)) return LH_ERR_UNSUPPORTED;
+  int nz = 0;
+  for (int z = 0; z < 3; ++z) nz = a.in[z] ? z + 1 : nz;
+  if (nz == 0) return LH_OK;
+  const int cpr = g.d / 8;
+  dim3 grid((unsigned)(g.n_c / a.spw), (unsigned)g.BH(), (unsigned)nz);
+  dim3 block((unsigned)(a.spw * a.R * cpr));
+  const size_t shm = (size_t)a.spw * a.R * (g.d + 1) * sizeof(float);
+  if (g.io == LH_BF16) {
+    if (g.d == 128) hipLaunchKernelGGL((pyr_score_kernel<bf16_t, 16>), grid, block, shm, st, a);
+    else hipLaunchKernelGGL((pyr_score_kernel<bf16_t, 8>), grid, block, shm, st, a);
+  } else {
+    if (g.d == 128) hipLaunchKernelGGL((pyr_score_kernel<float, 16>), grid, block, shm, st, a);
+    else hipLaunchKernelGGL((pyr_score_kernel<float, 8>), grid, block, shm, st, a);
+  }
+  return hip_status();
+}
+
+}  // namespace lh

@@ -1,0 +1,166 @@
+// Internal declarations shared by the HIP sources of liblighthouse.
+// Host geometry, element-type helpers and the kernel launchers each source
+// file provides.  Not part of the public ABI (include/lighthouse.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+#include "../../include/lighthouse.h"
+
+namespace lh {
+
+constexpr int kMaxLevels = 32;
+
+// Everything a kernel needs to know about one call's shapes.  Filled on the
+// host by make_geo() from a validated lh_dims and passed to kernels by value.
+struct Geo {
+  int64_t B, N, K, S, E, n_c, T, k_s, Bc, Sp;
+  int32_t H, d, p, L;
+  int32_t io, out;
+  float scale;                   // softmax scale (1/sqrt(d) when dims say 0)
+  int64_t lsize[kMaxLevels];     // N / p^l
+  int64_t loff[kMaxLevels];      // flat offset of level l
+  int64_t pw[kMaxLevels + 1];    // p^l
+  int64_t BH() const { return B * (int64_t)H; }
+};
+
+lh_status make_geo(const lh_dims *dims, Geo *g);
+
+inline size_t el_size(int32_t dt) { return dt == LH_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- device helpers
+typedef uint16_t bf16_t;   // raw bfloat16 bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// float32 -> bfloat16 with round-to-nearest-even (NaN kept quiet)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static float load(const float *p) { return *p; }
+  __device__ static float to_f32(float v) { return v; }
+  __device__ static float from_f32(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ static float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  __device__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// load / store 8 consecutive elements as float
+__device__ __forceinline__ void load8(const float *p, float *x) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16_t *p, float *x) {
+  const uint4 a = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void store8(float *p, const float *x) {
+  *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void store8(bf16_t *p, const float *x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// two-term bf16 split of 8 floats: hi = bf16(x), lo = bf16(x - hi), so that
+// hi + lo carries about 16 significant bits of x
+__device__ __forceinline__ void store8_split(bf16_t *hi, bf16_t *lo, const float *x) {
+  float h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = bf16_to_f32(f32_to_bf16(x[i]));
+    l[i] = x[i] - h[i];
+  }
+  store8(hi, h);
+  store8(lo, l);
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns LH_OK or LH_ERR_HIP / LH_ERR_UNSUPPORTED; none allocates.
+lh_status launch_pyramid_score(const Geo &g, const void *q, const void *k, const void *v,
+                               void *pq, void *pk, void *pv, float *sq, float *sk,
+                               hipStream_t st);
+lh_status check_pyramid_supported(const Geo &g);
+
+lh_status launch_select(const Geo &g, const float *sq, const float *sk, int32_t *sel_idx,
+                        int32_t *sel_anchor, uint8_t *sel_flags, int32_t *row_of,
+                        hipStream_t st);
+lh_status check_select_supported(const Geo &g);
+
+lh_status launch_gather(const Geo &g, const void *const src[3], const void *const psrc[3],
+                        const int32_t *sel_idx, void *const dst[3], hipStream_t st);
+// rows [BH, S, d] bf16 -> [BH, d, Sp] bf16 with zeroed padding
+lh_status launch_transpose(const Geo &g, const void *rows, void *tr, hipStream_t st);
+// os is float32; o has the output type
+lh_status launch_scatter(const Geo &g, const float *os, const int32_t *sel_anchor,
+                         const uint8_t *sel_flags, void *o, hipStream_t st);
+// Scatter adjoint.  dos (float32) may be NULL; dos_hi/dos_lo (bf16, may be
+// NULL) receive the two-term split dos ~= hi + lo; drow[j] = <dos_j, os_j>
+// when os (float32) and drow are not NULL.  dout has the output type.
+lh_status launch_scatter_bwd(const Geo &g, const void *dout, const int32_t *sel_anchor,
+                             const uint8_t *sel_flags, float *dos, bf16_t *dos_hi,
+                             bf16_t *dos_lo, const float *os, float *drow, hipStream_t st);
+lh_status launch_unpool(const Geo &g, const float *const dxs[3], const int32_t *row_of,
+                        void *const dx[3], hipStream_t st);
+
+// attention, float32 I/O (VALU)
+lh_status launch_attn_fwd_f32(const Geo &g, const float *qs, const float *ks, const float *vs,
+                              const uint8_t *flags, float *os, float *lse, hipStream_t st);
+lh_status launch_attn_bwd_f32(const Geo &g, const float *qs, const float *ks, const float *vs,
+                              const float *os, const float *lse, const uint8_t *flags,
+                              const float *dos, float *drow_ws, float *dqs, float *dks,
+                              float *dvs, hipStream_t st);
+
+// attention, bf16 I/O (MFMA).  vst/qst/kst/dost_*: transposed [BH, d, Sp].
+// dO enters the backward as a two-term bf16 split (hi + lo).
+lh_status launch_attn_fwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
+                               const bf16_t *vst, const uint8_t *flags, float *os, float *lse,
+                               hipStream_t st);
+lh_status launch_attn_bwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
+                               const bf16_t *vs, const bf16_t *qst, const bf16_t *kst,
+                               const bf16_t *dos_hi, const bf16_t *dos_lo,
+                               const bf16_t *dost_hi, const bf16_t *dost_lo, const float *lse,
+                               const float *drow, const uint8_t *flags, float *dqs,
+                               float *dks, float *dvs, hipStream_t st);
+lh_status launch_attn_bwd_dkv_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
+                                   const bf16_t *vs, const bf16_t *qst, const bf16_t *dos_hi,
+                                   const bf16_t *dos_lo, const bf16_t *dost_hi,
+                                   const bf16_t *dost_lo, const float *lse, const float *drow,
+                                   const uint8_t *flags, float *dks, float *dvs, hipStream_t st);
+lh_status launch_attn_bwd_dq_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
+                                  const bf16_t *vs, const bf16_t *kst, const bf16_t *dos_hi,
+                                  const bf16_t *dos_lo, const float *lse, const float *drow,
+                                  const uint8_t *flags, float *dqs, hipStream_t st);
+// float32 dos [BH,S,d] -> optional bf16 split (hi, lo) and drow = rowsum(dos * os)
+lh_status launch_dos_prep(const Geo &g, const float *dos, const float *os, bf16_t *dos_hi,
+                          bf16_t *dos_lo, float *drow, hipStream_t st);
+
+inline lh_status hip_status() {
+  return hipGetLastError() == hipSuccess ? LH_OK : LH_ERR_HIP;
+}
+
+inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+}  // namespace lh

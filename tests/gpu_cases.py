@@ -1,0 +1,102 @@
+"""Shared helpers of the GPU parity tests (not collected as tests).
+
+Each case is a seeded synthetic workload small enough for the float64 oracle
+to finish in seconds, spanning several kernel tiles and a ragged tail.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from oracle import lighthouse as orc
+from sparse_long_context_amd import synth
+
+
+@dataclass(frozen=True)
+class Case:
+    name: str
+    N: int
+    H: int
+    d: int
+    p: int
+    L: int
+    k_s: int
+    dtype: str = "bf16"
+    structure: str = "none"
+    out: str = "f32"          # output dtype of the parity run
+    seed: int = 1234
+
+    @property
+    def n_c(self):
+        return self.N // self.p ** (self.L - 1)
+
+    @property
+    def S(self):
+        return self.n_c * (self.k_s + 1)
+
+    @property
+    def K(self):
+        return self.n_c * self.k_s
+
+
+CASES = [
+    # the tiny float32 workload itself: N=4096, H=2, d=64, p=4, L=3, S=512
+    Case("tiny-f32", 4096, 2, 64, 4, 3, 1, dtype="f32", seed=synth.SEED_BASE + 1),
+    # d=128, S=1056: 8.25 query tiles of 128, ragged tail; spiky rows
+    Case("bf16-d128-ragged", 6144, 2, 128, 4, 4, 10, structure="spikes"),
+    # d=64, p=8, S=520 (ragged at 64); log-normal row scales
+    Case("bf16-d64-p8-ragged", 2560, 3, 64, 8, 3, 12, structure="lognormal"),
+    # every entry selected: the layer must equal dense causal SDPA
+    Case("bf16-full-selection", 1024, 2, 64, 4, 3, 20),
+    # K = 0: only the coarsest level
+    Case("bf16-coarsest-only", 4096, 2, 128, 4, 4, 0),
+    # L = 1: no pyramid, S = N
+    Case("bf16-L1-dense", 768, 1, 64, 2, 1, 0),
+    # bursts of high-norm tokens, d=128, bf16 outputs
+    Case("bf16-bursts-bf16out", 8192, 2, 128, 4, 5, 15, structure="bursts", out="bf16"),
+]
+
+
+def inputs(case: Case):
+    w = synth.Workload(0, case.name, case.N, case.H, case.d, case.p, case.L, case.S, case.dtype,
+                       case.structure)
+    return synth.make_inputs(w, seed=case.seed)
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def store_of(case: Case):
+    return "bf16" if case.dtype == "bf16" else "f32"
+
+
+def geometry(case: Case) -> orc.Geometry:
+    return orc.Geometry(case.N, case.p, case.L, case.K).check()
+
+
+def selection_from_gpu(g: orc.Geometry, sel_idx, anchor, flags, row_of) -> orc.Selection:
+    lev, _ = orc.entry_of_flat(g, sel_idx)
+    return orc.Selection(np.asarray(sel_idx, np.int64), np.asarray(anchor, np.int64), lev,
+                         np.asarray(flags, np.uint8), np.asarray(row_of, np.int64))
+
+
+def ulp_bf16(x):
+    """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
+    x = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def tol_for(case: Case, ref, out_dtype: str):
+    """Stated tolerance: max-abs 1e-5 for float32 I/O; 2e-2 for bf16 I/O
+    (plus half a bf16 step of the reference when the output is stored in
+    bf16)."""
+    if case.dtype == "f32":
+        return 1e-5
+    t = 2e-2
+    if out_dtype == "bf16":
+        return t + 0.5 * ulp_bf16(ref)
+    return t

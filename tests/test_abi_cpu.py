@@ -1,0 +1,126 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, and its host-side validation returns the documented codes without
+launching anything (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from sparse_long_context_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lighthouse.h")
+
+
+def header_symbols():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lh_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("liblighthouse.so not built (python -m sparse_long_context_amd.build)")
+    return L.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = header_symbols()
+    assert len(syms) >= 16
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(L.EXPORTS)
+    assert lib.lh_version().decode().count(".") == 2
+
+
+def dims(**kw):
+    base = dict(B=1, N=4096, H=2, d=64, p=4, L=3, K=256, S=512, io_dtype=L.LH_F32,
+                out_dtype=L.LH_F32, scale=0.0)
+    base.update(kw)
+    return L.Dims(base["B"], base["N"], base["H"], base["d"], base["p"], base["L"], base["K"],
+                  base["S"], base["io_dtype"], base["out_dtype"], base["scale"], 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, L.LH_OK),
+    (dict(io_dtype=L.LH_BF16, out_dtype=L.LH_BF16), L.LH_OK),
+    (dict(io_dtype=L.LH_BF16, out_dtype=L.LH_F32), L.LH_OK),
+    (dict(N=4100), L.LH_ERR_INVALID_ARG),             # N % p^(L-1)
+    (dict(K=255, S=511), L.LH_ERR_INVALID_ARG),       # K % n_c
+    (dict(K=256, S=513), L.LH_ERR_INVALID_ARG),       # S != K + n_c
+    (dict(K=21 * 256, S=22 * 256), L.LH_ERR_INVALID_ARG),   # k_s > T-1
+    (dict(K=20 * 256, S=21 * 256), L.LH_OK),          # k_s = T-1: everything selected
+    (dict(K=0, S=256), L.LH_OK),                      # coarsest only
+    (dict(p=1), L.LH_ERR_INVALID_ARG),
+    (dict(L=0), L.LH_ERR_INVALID_ARG),
+    (dict(B=0), L.LH_ERR_INVALID_ARG),
+    (dict(d=96), L.LH_ERR_UNSUPPORTED),
+    (dict(d=0), L.LH_ERR_INVALID_ARG),
+    (dict(io_dtype=7), L.LH_ERR_INVALID_ARG),
+    (dict(out_dtype=L.LH_BF16), L.LH_ERR_UNSUPPORTED),  # f32 in, bf16 out
+    (dict(scale=-1.0), L.LH_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), L.LH_ERR_INVALID_ARG),
+    (dict(N=2 ** 31, K=0, S=2 ** 27), L.LH_ERR_UNSUPPORTED),   # E >= 2^31
+    (dict(p=2, L=14, N=2 ** 14, K=0, S=2), L.LH_ERR_UNSUPPORTED),  # subtree too large
+])
+def test_validate(lib, kw, code):
+    assert lib.lh_validate(C.byref(dims(**kw))) == code
+
+
+def test_validate_null_and_reserved(lib):
+    assert lib.lh_validate(None) == L.LH_ERR_INVALID_ARG
+    d = dims()
+    d.reserved = 1
+    assert lib.lh_validate(C.byref(d)) == L.LH_ERR_INVALID_ARG
+
+
+def test_sizes_c4_shape(lib):
+    d = dims(N=131072, H=8, d=128, p=4, L=6, K=8064, S=8192, io_dtype=L.LH_BF16,
+             out_dtype=L.LH_BF16)
+    z = L.Sizes()
+    assert lib.lh_get_sizes(C.byref(d), C.byref(z)) == L.LH_OK
+    assert (z.E, z.n_c, z.T, z.k_s, z.Bc, z.Sp) == (174720, 128, 1365, 63, 1024, 8192)
+    assert z.pyramid_bytes == 8 * (174720 - 131072) * 128 * 2
+    assert z.score_bytes == 8 * 174720 * 4
+    assert z.token_io_bytes == 8 * 131072 * 128 * 2
+    assert z.ws_layer_fwd == 0 and z.ws_layer_bwd > 4 * 8 * 8192 * 128 * 4
+
+
+def test_ragged_sp(lib):
+    d = dims(N=2560, p=8, L=3, K=40 * 12, S=40 * 13, io_dtype=L.LH_BF16, out_dtype=L.LH_BF16)
+    z = L.Sizes()
+    assert lib.lh_get_sizes(C.byref(d), C.byref(z)) == L.LH_OK
+    assert z.Sp == 576
+
+
+def test_stage_calls_reject_bad_args_without_launch(lib):
+    d = dims()
+    P = C.c_void_p
+    # null pointers: rejected by host validation, nothing is launched
+    assert lib.lh_pyramid_score(C.byref(d), *([None] * 8), None) == L.LH_ERR_INVALID_ARG
+    assert lib.lh_topk_select(C.byref(d), *([None] * 6), None) == L.LH_ERR_INVALID_ARG
+    assert lib.lh_scatter(C.byref(d), *([None] * 4), None) == L.LH_ERR_INVALID_ARG
+    assert lib.lh_layer_fwd(C.byref(d), None, None, None, None, None, None, 0, None) == \
+        L.LH_ERR_INVALID_ARG
+    # misaligned pointer
+    bad = P(0x1003)
+    assert lib.lh_scatter(C.byref(d), bad, bad, bad, bad, None) == L.LH_ERR_INVALID_ARG
+    # invalid dims come first
+    dd = dims(N=4100)
+    assert lib.lh_scatter(C.byref(dd), P(0x1000), P(0x1000), P(0x1000), P(0x1000), None) == \
+        L.LH_ERR_INVALID_ARG
+    # missing workspace
+    d2 = dims(io_dtype=L.LH_BF16, out_dtype=L.LH_BF16)
+    p = P(0x10000)
+    assert lib.lh_subseq_attn_fwd(C.byref(d2), p, p, p, p, p, p, None, 0, None) == \
+        L.LH_ERR_WORKSPACE
+    s = L.Saved(*([0x10000] * 17))
+    assert lib.lh_layer_bwd(C.byref(d2), C.byref(s), p, p, p, p, None, 0, None) == \
+        L.LH_ERR_WORKSPACE
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -99):
+        assert len(lib.lh_status_string(s)) > 0

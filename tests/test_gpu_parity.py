@@ -1,0 +1,233 @@
+"""GPU parity of every stage and of the whole layer against the CPU oracle.
+
+Stage tests feed each kernel the GPU's own upstream outputs, so that a
+difference is located in the stage under test; the layer tests run
+lh_layer_fwd / lh_layer_bwd end to end from the inputs.  Integer outputs
+(scores' max inheritance, selection, indices, flags, row_of, gathers and
+scatters) must be bit-exact; floating point within the stated tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import lighthouse as orc
+from tests.gpu_cases import CASES, f64, geometry, inputs, selection_from_gpu, store_of, tol_for
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from sparse_long_context_amd import ops
+
+
+def _ctx(case, q):
+    out = torch.float32 if case.out == "f32" else torch.bfloat16
+    if case.dtype == "f32":
+        out = torch.float32
+    return ops.Ctx(ops.make_dims(q, case.p, case.L, case.S, out_dtype=out))
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _run_stages(case, dev):
+    Q, K, V, dO = (t.to(dev) for t in inputs(case))
+    c = _ctx(case, Q)
+    r = {"c": c, "Q": Q, "K": K, "V": V}
+    r["pq"], r["pk"], r["pv"], r["sq"], r["sk"] = ops.pyramid_score(c, Q, K, V)
+    r["sel_idx"], r["anchor"], r["flags"], r["row_of"] = ops.topk_select(c, r["sq"], r["sk"])
+    bf = case.dtype == "bf16"
+    g = ops.gather(c, Q, K, V, r["pq"], r["pk"], r["pv"], r["sel_idx"], transposed=bf)
+    r["qs"], r["ks"], r["vs"] = g[:3]
+    if bf:
+        r["qst"], r["kst"], r["vst"] = g[3:]
+    r["os"], r["lse"] = ops.subseq_attn_fwd(c, r["qs"], r["ks"], r["vs"], r["flags"])
+    r["o"] = ops.scatter(c, r["os"], r["anchor"], r["flags"])
+    r["dO"] = dO.to(dev, c.out)
+    r["dos"] = ops.scatter_bwd(c, r["dO"], r["anchor"], r["flags"])
+    r["dqs"], r["dks"], r["dvs"] = ops.subseq_attn_bwd(c, r["qs"], r["ks"], r["vs"], r["os"],
+                                                       r["lse"], r["flags"], r["dos"])
+    r["dq"], r["dk"], r["dv"] = ops.gather_bwd(c, r["dqs"], r["dks"], r["dvs"], r["row_of"])
+    torch.cuda.synchronize()
+    return r
+
+
+_cache = {}
+
+
+def stages(case, dev):
+    if case.name not in _cache:
+        print(f"[gpu] stages {case.name}", flush=True)
+        _cache[case.name] = _run_stages(case, dev)
+    return _cache[case.name]
+
+
+ids = [c.name for c in CASES]
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_pyramid_and_scores(case, dev):
+    r = stages(case, dev)
+    g = geometry(case)
+    for h in range(case.H):
+        Qh, Kh, Vh = (f64(r[n][0, h]) for n in ("Q", "K", "V"))
+        sQ, sK = orc.scores(Qh, Kh, g)
+        assert np.array_equal(r["sq"][0, h].cpu().numpy(), sQ), "sq differs"
+        assert np.array_equal(r["sk"][0, h].cpu().numpy(), sK), "sk differs"
+        if case.L == 1:
+            continue
+        for X, P in ((Qh, "pq"), (Kh, "pk"), (Vh, "pv")):
+            want = np.concatenate(orc.pyramid(X, g, store=store_of(case))[1:])
+            got = f64(r[P][0, h])
+            if case.dtype == "bf16":
+                # one rounding of a float32 sum: at most one bf16 step from the
+                # rounded exact mean, and almost always equal to it
+                exact = np.concatenate(orc.pyramid(X, g)[1:])
+                step = np.maximum(np.abs(exact), 1e-30) * 2.0 ** -7
+                assert np.all(np.abs(got - want) <= step * 1.0001)
+                assert np.mean(got != want) < 1e-3
+            else:
+                np.testing.assert_allclose(got, want, rtol=2e-7, atol=1e-7)
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_selection_bit_exact(case, dev):
+    r = stages(case, dev)
+    g = geometry(case)
+    for h in range(case.H):
+        sig = orc.sigma(r["sq"][0, h].cpu().numpy(), r["sk"][0, h].cpu().numpy())
+        sel = orc.select(sig, g)
+        assert np.array_equal(r["sel_idx"][0, h].cpu().numpy(), sel.sel_idx)
+        assert np.array_equal(r["anchor"][0, h].cpu().numpy(), sel.sel_anchor)
+        assert np.array_equal(r["flags"][0, h].cpu().numpy(), sel.sel_flags)
+        assert np.array_equal(r["row_of"][0, h].cpu().numpy(), sel.row_of)
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_gather_and_transposes(case, dev):
+    r = stages(case, dev)
+    S = case.S
+    for h in range(case.H):
+        for X, P, XS in (("Q", "pq", "qs"), ("K", "pk", "ks"), ("V", "pv", "vs")):
+            rows = r[X][0, h] if case.L == 1 else torch.cat([r[X][0, h], r[P][0, h]])
+            want = rows[r["sel_idx"][0, h].long()]
+            assert torch.equal(r[XS][0, h], want)
+        if case.dtype == "bf16":
+            for XS, XT in (("qs", "qst"), ("ks", "kst"), ("vs", "vst")):
+                t = r[XT][0, h]
+                assert torch.equal(t[:, :S], r[XS][0, h].t())
+                assert torch.all(t[:, S:] == 0)
+
+
+def _close(got, want, tol, what):
+    err = np.abs(got - want)
+    worst = float(np.max(err - tol)) if err.size else -1.0
+    print(f"[parity] {what}: max|err| {float(err.max()) if err.size else 0:.3e}", flush=True)
+    assert worst <= 0, f"{what}: exceeds tolerance by {worst:.3e}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_attention_fwd(case, dev):
+    r = stages(case, dev)
+    c = r["c"]
+    for h in range(case.H):
+        OS, LSE = orc.attention_fwd(f64(r["qs"][0, h]), f64(r["ks"][0, h]), f64(r["vs"][0, h]),
+                                    r["flags"][0, h].cpu().numpy(), c.dims.scale or 1 / np.sqrt(case.d))
+        _close(f64(r["os"][0, h]), OS, tol_for(case, OS, case.out), f"{case.name} h{h} OS")
+        _close(f64(r["lse"][0, h]), LSE, 1e-4 if case.dtype == "f32" else 2e-3, f"{case.name} h{h} LSE")
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_scatter_and_adjoint(case, dev):
+    r = stages(case, dev)
+    g = geometry(case)
+    for h in range(case.H):
+        sel = selection_from_gpu(g, *(r[n][0, h].cpu().numpy() for n in ("sel_idx", "anchor", "flags", "row_of")))
+        src = orc.hold_source(sel, case.N)
+        os_ = r["os"][0, h]
+        want = torch.zeros_like(r["o"][0, h])
+        ok = torch.from_numpy(src >= 0)
+        want[ok.to(dev)] = os_[torch.from_numpy(src[src >= 0]).to(dev)].to(want.dtype)
+        assert torch.equal(r["o"][0, h], want), "scatter is a pure copy"
+        dOS = orc.scatter_adjoint(f64(r["dO"][0, h]), sel, case.N)
+        got = f64(r["dos"][0, h])
+        scale = 1e-5 * (1 + np.abs(dOS))
+        assert np.all(np.abs(got - dOS) <= scale), float(np.max(np.abs(got - dOS)))
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_attention_bwd(case, dev):
+    r = stages(case, dev)
+    c = r["c"]
+    scale = c.dims.scale or 1 / np.sqrt(case.d)
+    for h in range(case.H):
+        dQS, dKS, dVS = orc.attention_bwd(f64(r["qs"][0, h]), f64(r["ks"][0, h]), f64(r["vs"][0, h]),
+                                          r["flags"][0, h].cpu().numpy(), scale, f64(r["dos"][0, h]))
+        for n, want in (("dqs", dQS), ("dks", dKS), ("dvs", dVS)):
+            _close(f64(r[n][0, h]), want, tol_for(case, want, "f32"), f"{case.name} h{h} {n}")
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_unpool(case, dev):
+    r = stages(case, dev)
+    g = geometry(case)
+    for h in range(case.H):
+        sel = selection_from_gpu(g, *(r[n][0, h].cpu().numpy() for n in ("sel_idx", "anchor", "flags", "row_of")))
+        for n, o in (("dqs", "dq"), ("dks", "dk"), ("dvs", "dv")):
+            want = orc.pool_adjoint(orc.gather_adjoint(f64(r[n][0, h]), sel, g), g)
+            got = f64(r[o][0, h])
+            if case.out == "bf16" and case.dtype == "bf16":
+                tol = 1e-5 * (1 + np.abs(want)) + np.abs(want) * 2.0 ** -8
+            else:
+                tol = 1e-5 * (1 + np.abs(want))
+            assert np.all(np.abs(got - want) <= tol), float(np.max(np.abs(got - want)))
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_layer_vs_oracle(case, dev):
+    """lh_layer_fwd/bwd end to end against the oracle run from the inputs."""
+    Q, K, V, dO = (t.to(dev) for t in inputs(case))
+    c = _ctx(case, Q)
+    o, saved = ops.layer_fwd(c, Q, K, V)
+    dOc = dO.to(c.out)
+    dq, dk, dv = ops.layer_bwd(c, saved, dOc)
+    torch.cuda.synchronize()
+    g = geometry(case)
+    for h in range(case.H):
+        fw = orc.head_forward(f64(Q[0, h]), f64(K[0, h]), f64(V[0, h]), g, store=store_of(case))
+        assert np.array_equal(saved["sel_idx"][0, h].cpu().numpy(), fw.sel.sel_idx)
+        _close(f64(o[0, h]), fw.O, tol_for(case, fw.O, case.out), f"{case.name} h{h} O")
+        gq, gk, gv = orc.head_backward(fw, f64(dOc[0, h]))[:3]
+        for got, want, n in ((dq, gq, "dQ"), (dk, gk, "dK"), (dv, gv, "dV")):
+            _close(f64(got[0, h]), want, tol_for(case, want, case.out), f"{case.name} h{h} {n}")
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_layer_matches_stages_and_is_deterministic(case, dev):
+    r = stages(case, dev)
+    c = r["c"]
+    o1, s1 = ops.layer_fwd(c, r["Q"], r["K"], r["V"])
+    o2, s2 = ops.layer_fwd(c, r["Q"], r["K"], r["V"])
+    g1 = ops.layer_bwd(c, s1, r["dO"])
+    g2 = ops.layer_bwd(c, s2, r["dO"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and all(torch.equal(a, b) for a, b in zip(g1, g2))
+    assert torch.equal(o1, r["o"])
+    for a, n in zip(g1, ("dq", "dk", "dv")):
+        assert torch.equal(a, r[n]), n
+
+
+def test_full_selection_is_dense_sdpa(dev):
+    """With every entry selected the layer is dense causal SDPA (float32
+    reference on the CPU)."""
+    case = [c for c in CASES if c.name == "bf16-full-selection"][0]
+    Q, K, V, _ = inputs(case)
+    c = _ctx(case, Q.to(dev))
+    o, _ = ops.layer_fwd(c, Q.to(dev), K.to(dev), V.to(dev))
+    ref = torch.nn.functional.scaled_dot_product_attention(Q.double(), K.double(), V.double(),
+                                                           is_causal=True)
+    err = (o.double().cpu() - ref).abs().max().item()
+    print(f"[parity] full selection vs SDPA: {err:.3e}", flush=True)
+    assert err < 2e-2
