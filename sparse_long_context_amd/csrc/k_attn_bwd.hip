@@ -102,26 +102,25 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
       const int idx = i * 256 + tid;
       const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
       const int64_t qq = q0 + r;
-      uint4 a = make_uint4(0, 0, 0, 0), b = a, e = a;
-      if (qq < S) {
-        a = *reinterpret_cast<const uint4 *>(Q + qq * D + c8);
-        b = *reinterpret_cast<const uint4 *>(dOH + qq * D + c8);
-        e = *reinterpret_cast<const uint4 *>(dOL + qq * D + c8);
-      }
-      *reinterpret_cast<uint4 *>(&sm.q[r][c8]) = a;
-      *reinterpret_cast<uint4 *>(&sm.dOh[r][c8]) = b;
-      *reinterpret_cast<uint4 *>(&sm.dOl[r][c8]) = e;
+      // rows past S repeat row S-1: their lse2 is +inf, so P = dS = 0
+      const int64_t qc = min(qq, S - 1);
+      const u32x4 a = *reinterpret_cast<const u32x4 *>(Q + qc * D + c8);
+      const u32x4 b = *reinterpret_cast<const u32x4 *>(dOH + qc * D + c8);
+      const u32x4 e = *reinterpret_cast<const u32x4 *>(dOL + qc * D + c8);
+      *reinterpret_cast<u32x4 *>(&sm.q[r][c8]) = a;
+      *reinterpret_cast<u32x4 *>(&sm.dOh[r][c8]) = b;
+      *reinterpret_cast<u32x4 *>(&sm.dOl[r][c8]) = e;
     }
 #pragma unroll
     for (int i = 0; i < TPASS; ++i) {
       const int idx = i * 256 + tid;
       const int r = idx / (kKvBQ / 8), c8 = (idx % (kKvBQ / 8)) * 8;
-      *reinterpret_cast<uint4 *>(&sm.qt[r][c8]) =
-          *reinterpret_cast<const uint4 *>(Qt + (int64_t)r * Sp + q0 + c8);
-      *reinterpret_cast<uint4 *>(&sm.dOth[r][c8]) =
-          *reinterpret_cast<const uint4 *>(dOtH + (int64_t)r * Sp + q0 + c8);
-      *reinterpret_cast<uint4 *>(&sm.dOtl[r][c8]) =
-          *reinterpret_cast<const uint4 *>(dOtL + (int64_t)r * Sp + q0 + c8);
+      *reinterpret_cast<u32x4 *>(&sm.qt[r][c8]) =
+          *reinterpret_cast<const u32x4 *>(Qt + (int64_t)r * Sp + q0 + c8);
+      *reinterpret_cast<u32x4 *>(&sm.dOth[r][c8]) =
+          *reinterpret_cast<const u32x4 *>(dOtH + (int64_t)r * Sp + q0 + c8);
+      *reinterpret_cast<u32x4 *>(&sm.dOtl[r][c8]) =
+          *reinterpret_cast<const u32x4 *>(dOtL + (int64_t)r * Sp + q0 + c8);
     }
     if (tid < kKvBQ) {
       const int64_t qq = q0 + tid;
@@ -134,20 +133,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     if (all_dead || q0 + kKvBQ - 1 < kw0) continue;
     const bool diag = q0 < kw0 + 32;
 
-    f32x16 acc_p[2], acc_ds[2];
-#pragma unroll
+    // the block's two 32-query halves one after the other: S and dP of a
+    // half (lane: key column; rows: queries qq*32 + 8I + 4h + J) feed dV and
+    // dK at once, so only one half's logits are live
+#pragma unroll 1
     for (int qq = 0; qq < 2; ++qq) {
       f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         const bf16x8 aq = ld_bf16x8(&sm.q[qq * 32 + col][s * 16 + 8 * h]);
+        sacc = mfma32(aq, kreg[s], sacc);
+      }
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
         const bf16x8 adh = ld_bf16x8(&sm.dOh[qq * 32 + col][s * 16 + 8 * h]);
         const bf16x8 adl = ld_bf16x8(&sm.dOl[qq * 32 + col][s * 16 + 8 * h]);
-        sacc = mfma32(aq, kreg[s], sacc);
         dpacc = mfma32(adh, vreg[s], dpacc);
         dpacc = mfma32(adl, vreg[s], dpacc);
       }
-      // lane: key column; rows are queries qq*32 + 8I + 4h + J
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int ql = qq * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
@@ -156,28 +159,27 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
         sacc[v] = p;
         dpacc[v] = p * (dpacc[v] - sm.drow[ql]);
       }
-      acc_p[qq] = sacc;
-      acc_ds[qq] = dpacc;
-    }
-    // dV += P^T dO, dK += dS^T Q over four 16-query steps
+      // dV += P^T dO, dK += dS^T Q over the half's two 16-query steps
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 aph, apl, ash, asl;
-      pack_split(acc_p[s >> 1], 8 * (s & 1), aph, apl);
-      pack_split(acc_ds[s >> 1], 8 * (s & 1), ash, asl);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int s = 2 * qq + s2;
+        bf16x8 aph, apl, ash, asl;
+        pack_split(sacc, 8 * s2, aph, apl);
+        pack_split(dpacc, 8 * s2, ash, asl);
 #pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const bf16_t *rdh = &sm.dOth[b * 32 + col][0];
-        const bf16_t *rdl = &sm.dOtl[b * 32 + col][0];
-        const bf16_t *rq = &sm.qt[b * 32 + col][0];
-        const bf16x8 bdh = ld_bf16x4x2(rdh + 16 * s + 4 * h, rdh + 16 * s + 8 + 4 * h);
-        const bf16x8 bdl = ld_bf16x4x2(rdl + 16 * s + 4 * h, rdl + 16 * s + 8 + 4 * h);
-        const bf16x8 bq = ld_bf16x4x2(rq + 16 * s + 4 * h, rq + 16 * s + 8 + 4 * h);
-        acc_dv[b] = mfma32(aph, bdh, acc_dv[b]);
-        acc_dv[b] = mfma32(aph, bdl, acc_dv[b]);
-        acc_dv[b] = mfma32(apl, bdh, acc_dv[b]);
-        acc_dk[b] = mfma32(ash, bq, acc_dk[b]);
-        acc_dk[b] = mfma32(asl, bq, acc_dk[b]);
+        for (int b = 0; b < DB; ++b) {
+          const bf16_t *rdh = &sm.dOth[b * 32 + col][0];
+          const bf16_t *rdl = &sm.dOtl[b * 32 + col][0];
+          const bf16_t *rq = &sm.qt[b * 32 + col][0];
+          const bf16x8 bdh = ld_bf16x4x2(rdh + 16 * s + 4 * h, rdh + 16 * s + 8 + 4 * h);
+          const bf16x8 bdl = ld_bf16x4x2(rdl + 16 * s + 4 * h, rdl + 16 * s + 8 + 4 * h);
+          const bf16x8 bq = ld_bf16x4x2(rq + 16 * s + 4 * h, rq + 16 * s + 8 + 4 * h);
+          acc_dv[b] = mfma32(aph, bdh, acc_dv[b]);
+          acc_dv[b] = mfma32(aph, bdl, acc_dv[b]);
+          acc_dv[b] = mfma32(apl, bdh, acc_dv[b]);
+          acc_dk[b] = mfma32(ash, bq, acc_dk[b]);
+          acc_dk[b] = mfma32(asl, bq, acc_dk[b]);
+        }
       }
     }
   }
@@ -260,21 +262,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     for (int i = 0; i < RPASS; ++i) {
       const int idx = i * 256 + tid;
       const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-      const int64_t kk = k0 + r;
-      uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-      if (kk < S) {
-        a = *reinterpret_cast<const uint4 *>(Kg + kk * D + c8);
-        b = *reinterpret_cast<const uint4 *>(Vg + kk * D + c8);
-      }
-      *reinterpret_cast<uint4 *>(&sm.k[r][c8]) = a;
-      *reinterpret_cast<uint4 *>(&sm.v[r][c8]) = b;
+      // rows past S repeat row S-1: those keys carry a -inf bias
+      const int64_t kk = min(k0 + r, S - 1);
+      *reinterpret_cast<u32x4 *>(&sm.k[r][c8]) = *reinterpret_cast<const u32x4 *>(Kg + kk * D + c8);
+      *reinterpret_cast<u32x4 *>(&sm.v[r][c8]) = *reinterpret_cast<const u32x4 *>(Vg + kk * D + c8);
     }
 #pragma unroll
     for (int i = 0; i < TPASS; ++i) {
       const int idx = i * 256 + tid;
       const int r = idx / (kQBK / 8), c8 = (idx % (kQBK / 8)) * 8;
-      *reinterpret_cast<uint4 *>(&sm.kt[r][c8]) =
-          *reinterpret_cast<const uint4 *>(Kt + (int64_t)r * Sp + k0 + c8);
+      *reinterpret_cast<u32x4 *>(&sm.kt[r][c8]) =
+          *reinterpret_cast<const u32x4 *>(Kt + (int64_t)r * Sp + k0 + c8);
     }
     if (tid < kQBK) {
       const int64_t kk = k0 + tid;

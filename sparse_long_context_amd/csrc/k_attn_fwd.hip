@@ -70,53 +70,55 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
   const int64_t kend = min(S, (int64_t)(qb + 1) * kFwdBM);
   const int nkb = (int)((kend + kFwdBN - 1) / kFwdBN);
 
-  uint4 kpre[KPASS], vpre[VPASS];
+  u32x4 kpre[KPASS], vpre[VPASS];
   float bpre = 0.f;
-  auto prefetch = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      const int idx = i * 256 + tid;
-      const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-      const int64_t key = (int64_t)kb * kFwdBN + r;
-      kpre[i] = key < S ? *reinterpret_cast<const uint4 *>(Kg + key * D + c8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VPASS; ++i) {
-      const int idx = i * 256 + tid;
-      const int r = idx / (kFwdBN / 8), c8 = (idx % (kFwdBN / 8)) * 8;
-      vpre[i] = *reinterpret_cast<const uint4 *>(Vt + (int64_t)r * Sp + (int64_t)kb * kFwdBN + c8);
-    }
-    if (tid < kFwdBN) {
-      const int64_t key = (int64_t)kb * kFwdBN + tid;
-      bpre = (key < S && !(fl[key] & LH_ROW_REDUNDANT)) ? 0.f : -INFINITY;
-    }
-  };
-  auto commit = [&]() {
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      const int idx = i * 256 + tid;
-      const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-      *reinterpret_cast<uint4 *>(&sm.k[r][c8]) = kpre[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPASS; ++i) {
-      const int idx = i * 256 + tid;
-      const int r = idx / (kFwdBN / 8), c8 = (idx % (kFwdBN / 8)) * 8;
-      *reinterpret_cast<uint4 *>(&sm.vt[r][c8]) = vpre[i];
-    }
-    if (tid < kFwdBN) sm.bias[tid] = bpre;
-  };
+  // global -> registers for key block kb
+#define LH_FWD_PREFETCH(kb)                                                                  \
+  do {                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < KPASS; ++i) {                                     \
+      const int idx = i * 256 + tid;                                                         \
+      const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;                                 \
+      /* rows past S repeat row S-1: their keys carry a -inf bias */                       \
+      const int64_t key = min((int64_t)(kb) * kFwdBN + r, S - 1);                            \
+      kpre[i] = *reinterpret_cast<const u32x4 *>(Kg + key * D + c8);                            \
+    }                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < VPASS; ++i) {                                     \
+      const int idx = i * 256 + tid;                                                         \
+      const int r = idx / (kFwdBN / 8), c8 = (idx % (kFwdBN / 8)) * 8;                       \
+      vpre[i] = *reinterpret_cast<const u32x4 *>(Vt + (int64_t)r * Sp +                      \
+                                                 (int64_t)(kb) * kFwdBN + c8);               \
+    }                                                                                        \
+    if (tid < kFwdBN) {                                                                      \
+      const int64_t key = (int64_t)(kb) * kFwdBN + tid;                                      \
+      bpre = (key < S && !(fl[key] & LH_ROW_REDUNDANT)) ? 0.f : -INFINITY;                   \
+    }                                                                                        \
+  } while (0)
+  // registers -> LDS
+#define LH_FWD_COMMIT()                                                                      \
+  do {                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < KPASS; ++i) {                                     \
+      const int idx = i * 256 + tid;                                                         \
+      const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;                                 \
+      *reinterpret_cast<u32x4 *>(&sm.k[r][c8]) = kpre[i];                                    \
+    }                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < VPASS; ++i) {                                     \
+      const int idx = i * 256 + tid;                                                         \
+      const int r = idx / (kFwdBN / 8), c8 = (idx % (kFwdBN / 8)) * 8;                       \
+      *reinterpret_cast<u32x4 *>(&sm.vt[r][c8]) = vpre[i];                                   \
+    }                                                                                        \
+    if (tid < kFwdBN) sm.bias[tid] = bpre;                                                   \
+  } while (0)
 
   f32x16 acc_o[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc_o[b] = zero16();
   float m_run = -INFINITY, l_half = 0.f;
 
-  prefetch(0);
-  commit();
+  LH_FWD_PREFETCH(0);
+  LH_FWD_COMMIT();
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) prefetch(kb + 1);
+    if (kb + 1 < nkb) LH_FWD_PREFETCH(kb + 1);
     const int64_t k0 = (int64_t)kb * kFwdBN;
     if (k0 <= q0w + 31) {          // some key of the block is visible to this wavefront
       f32x16 acc_s[2];
@@ -177,11 +179,13 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
     }
     __syncthreads();
     if (kb + 1 < nkb) {
-      commit();
+      LH_FWD_COMMIT();
       __syncthreads();
     }
   }
 
+#undef LH_FWD_PREFETCH
+#undef LH_FWD_COMMIT
   const float l_tot = l_half + __shfl_xor(l_half, 32);
   if (q < S) {
     const float inv = 1.f / l_tot;

@@ -15,6 +15,7 @@
 namespace lh {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16 raw bytes
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
