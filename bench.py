@@ -192,13 +192,13 @@ def main():
         timed("attn_fwd_mfma", lambda: ops.attn_fwd_mfma(c, r["qs"], r["ks"], r["vst"], r["fl"], os_, lse))
         timed("scatter", lambda: ops.scatter(c, os_, r["anc"], r["fl"]))
         dos = timed("scatter_bwd", lambda: ops.scatter_bwd(c, dO, r["anc"], r["fl"]))
-        hi, lo, thi, tlo, drow = timed("attn_bwd_prep", lambda: ops.attn_bwd_prep(c, dos, os_))
+        hi, lo, drow = timed("attn_bwd_prep", lambda: ops.attn_bwd_prep(c, dos, os_))
         dks = torch.empty(w.B, w.H, S, w.d, dtype=torch.float32, device=dev)
         dvs, dqs = torch.empty_like(dks), torch.empty_like(dks)
-        timed("attn_bwd_dkv_mfma", lambda: ops.attn_bwd_dkv_mfma(c, r["qs"], r["ks"], r["vs"], r["qst"], hi, lo,
-                                                                 thi, tlo, lse, drow, r["fl"], dks, dvs))
-        timed("attn_bwd_dq_mfma", lambda: ops.attn_bwd_dq_mfma(c, r["qs"], r["ks"], r["vs"], r["kst"], hi, lo,
-                                                               lse, drow, r["fl"], dqs))
+        timed("attn_bwd_dkv_mfma", lambda: ops.attn_bwd_dkv_mfma(c, r["qs"], r["ks"], r["vs"], hi, lo, lse,
+                                                                 drow, r["fl"], dks, dvs))
+        timed("attn_bwd_dq_mfma", lambda: ops.attn_bwd_dq_mfma(c, r["qs"], r["ks"], r["vs"], hi, lo, lse, drow,
+                                                               r["fl"], dqs))
         timed("gather_bwd", lambda: ops.gather_bwd(c, dqs, dks, dvs, r["row_of"]))
         # dominant kernel: the single-kernel stage with the largest time
         name = max((n for n in stages if n in KERNEL_OF), key=lambda n: stages[n]["ms"])

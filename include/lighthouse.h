@@ -103,8 +103,12 @@ typedef struct lh_dims {
  *   row_of       [B,H,E]     int32     subsequence row of each entry, -1 if
  *                                      unselected
  *   qs, ks, vs   [B,H,S,d]   io_dtype  gathered subsequence
- *   qst,kst,vst  [B,H,d,Sp]  io_dtype  transposed copies of qs, ks, vs
- *                                      (LH_BF16 I/O only; NULL for LH_F32)
+ *   vst          [B,H,d,Sp]  io_dtype  transposed copy of vs (LH_BF16 I/O;
+ *                                      NULL for LH_F32)
+ *   qst, kst                           unused by the layer calls (may be
+ *                                      NULL); kept so callers can hold the
+ *                                      other transposed copies lh_gather
+ *                                      writes
  *   os           [B,H,S,d]   float32   subsequence attention output (kept
  *                                      in float32: the backward's
  *                                      rowsum(dOS * OS) needs it unrounded)
@@ -227,36 +231,32 @@ lh_status lh_subseq_attn_bwd(const lh_dims *dims, const void *qs,
                              float *dvs, void *ws, size_t ws_bytes,
                              lh_stream stream);
 
-/* ---- stage 3b, operand-prepared forms: each launches exactly one MFMA
- * kernel (LH_BF16 I/O only; LH_ERR_UNSUPPORTED otherwise).  They take the
- * operand layouts the kernels read directly, for callers that keep those
- * buffers themselves, and for per-kernel timing.
- *   vst, qst, kst         [B,H,d,Sp] bf16 transposed copies (zero padding)
+/* ---- stage 3b, operand-prepared forms: each of the three MFMA calls
+ * launches exactly one kernel (LH_BF16 I/O only; LH_ERR_UNSUPPORTED
+ * otherwise).  They take the operand layouts the kernels read directly, for
+ * callers that keep those buffers themselves, and for per-kernel timing.
+ *   vst                   [B,H,d,Sp] bf16 transposed copy of vs (zero padding)
  *   dos_hi, dos_lo        [B,H,S,d]  bf16 two-term split of dOS (hi + lo)
- *   dost_hi, dost_lo      [B,H,d,Sp] their transposed copies
  *   drow                  [B,H,S]    float32 rowsum(dOS * OS)
+ * lh_attn_bwd_prep:     dos (float32 [B,H,S,d]) and os (float32) -> dos_hi,
+ *                       dos_lo, drow
  * lh_attn_fwd_mfma:     os [B,H,S,d] float32, lse [B,H,S] (as lh_subseq_attn_fwd)
  * lh_attn_bwd_dkv_mfma: dks, dvs [B,H,S,d] float32
  * lh_attn_bwd_dq_mfma:  dqs [B,H,S,d] float32 */
-/* Operands of the two backward kernels from dOS (float32 [B,H,S,d]) and OS
- * (float32): dos_hi/dos_lo, their transposes dost_hi/dost_lo, and drow. */
 lh_status lh_attn_bwd_prep(const lh_dims *dims, const float *dos, const float *os,
-                           void *dos_hi, void *dos_lo, void *dost_hi, void *dost_lo,
-                           float *drow, lh_stream stream);
+                           void *dos_hi, void *dos_lo, float *drow, lh_stream stream);
 lh_status lh_attn_fwd_mfma(const lh_dims *dims, const void *qs, const void *ks,
                            const void *vst, const uint8_t *sel_flags, float *os,
                            float *lse, lh_stream stream);
 lh_status lh_attn_bwd_dkv_mfma(const lh_dims *dims, const void *qs, const void *ks,
-                               const void *vs, const void *qst, const void *dos_hi,
-                               const void *dos_lo, const void *dost_hi,
-                               const void *dost_lo, const float *lse,
-                               const float *drow, const uint8_t *sel_flags,
-                               float *dks, float *dvs, lh_stream stream);
+                               const void *vs, const void *dos_hi, const void *dos_lo,
+                               const float *lse, const float *drow,
+                               const uint8_t *sel_flags, float *dks, float *dvs,
+                               lh_stream stream);
 lh_status lh_attn_bwd_dq_mfma(const lh_dims *dims, const void *qs, const void *ks,
-                              const void *vs, const void *kst, const void *dos_hi,
-                              const void *dos_lo, const float *lse,
-                              const float *drow, const uint8_t *sel_flags,
-                              float *dqs, lh_stream stream);
+                              const void *vs, const void *dos_hi, const void *dos_lo,
+                              const float *lse, const float *drow,
+                              const uint8_t *sel_flags, float *dqs, lh_stream stream);
 
 /* ---- stage 4: scatter-back (explainer 2.C: a deterministic kernel puts the
  * outputs back at their positions) ----

@@ -57,10 +57,10 @@ _PROTOS = {
     "lh_gather": [_P] * 13 + [_P],
     "lh_subseq_attn_fwd": [_P] * 6 + [_P, C.c_size_t, _P],
     "lh_subseq_attn_bwd": [_P] * 10 + [_P, C.c_size_t, _P],
-    "lh_attn_bwd_prep": [_P] * 7 + [_P],
+    "lh_attn_bwd_prep": [_P] * 5 + [_P],
     "lh_attn_fwd_mfma": [_P] * 6 + [_P],
-    "lh_attn_bwd_dkv_mfma": [_P] * 13 + [_P],
-    "lh_attn_bwd_dq_mfma": [_P] * 10 + [_P],
+    "lh_attn_bwd_dkv_mfma": [_P] * 10 + [_P],
+    "lh_attn_bwd_dq_mfma": [_P] * 9 + [_P],
     "lh_scatter": [_P] * 4 + [_P],
     "lh_scatter_bwd": [_P] * 4 + [_P],
     "lh_gather_bwd": [_P] * 7 + [_P],

@@ -81,13 +81,12 @@ static size_t rows_bf16(const Geo &g) { return (size_t)g.BH() * g.S * g.d * 2; }
 static size_t ws_attn_bwd(const Geo &g) {
   Sizes z = sizes_of(g);
   if (g.io == LH_F32) return al256(z.drow);
-  // dos split (hi, lo) rows and transposes, qs^T, ks^T, drow
-  return 2 * al256(rows_bf16(g)) + 4 * al256(z.subseq_t) + al256(z.drow);
+  return 2 * al256(rows_bf16(g)) + al256(z.drow);        // dos split (hi, lo), drow
 }
 static size_t ws_layer_bwd(const Geo &g) {
   Sizes z = sizes_of(g);
   size_t b = 3 * al256(z.subseq_f32) + al256(z.drow);   // dqs, dks, dvs, drow
-  if (g.io == LH_BF16) b += 2 * al256(rows_bf16(g)) + 2 * al256(z.subseq_t);
+  if (g.io == LH_BF16) b += 2 * al256(rows_bf16(g));     // dos split
   else b += al256(z.subseq_f32);                          // float32 dos
   return b;
 }
@@ -284,35 +283,23 @@ lh_status lh_subseq_attn_bwd(const lh_dims *dims, const void *qs, const void *ks
   }
   bf16_t *dhi = (bf16_t *)c.take(rows_bf16(g));
   bf16_t *dlo = (bf16_t *)c.take(rows_bf16(g));
-  bf16_t *dthi = (bf16_t *)c.take(z.subseq_t);
-  bf16_t *dtlo = (bf16_t *)c.take(z.subseq_t);
-  bf16_t *qst = (bf16_t *)c.take(z.subseq_t);
-  bf16_t *kst = (bf16_t *)c.take(z.subseq_t);
   float *drow = (float *)c.take(z.drow);
   if (!c.ok()) return LH_ERR_WORKSPACE;
   LH_TRY(launch_dos_prep(g, dos, (const float *)os, dhi, dlo, drow, st));
-  LH_TRY(launch_transpose(g, dhi, dthi, st));
-  LH_TRY(launch_transpose(g, dlo, dtlo, st));
-  LH_TRY(launch_transpose(g, qs, qst, st));
-  LH_TRY(launch_transpose(g, ks, kst, st));
   return launch_attn_bwd_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
-                              qst, kst, dhi, dlo, dthi, dtlo, lse, drow, sel_flags, dqs, dks,
-                              dvs, st);
+                              dhi, dlo, lse, drow, sel_flags, dqs, dks, dvs, st);
 }
 
 lh_status lh_attn_bwd_prep(const lh_dims *dims, const float *dos, const float *os, void *dos_hi,
-                           void *dos_lo, void *dost_hi, void *dost_lo, float *drow,
-                           lh_stream stream) {
+                           void *dos_lo, float *drow, lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
   if (g.io != LH_BF16) return LH_ERR_UNSUPPORTED;
-  LH_REQ(dos && os && dos_hi && dos_lo && dost_hi && dost_lo && drow);
+  LH_REQ(dos && os && dos_hi && dos_lo && drow);
   LH_REQ(aligned16(dos) && aligned16(os) && aligned16(dos_hi) && aligned16(dos_lo) &&
-         aligned16(dost_hi) && aligned16(dost_lo) && aligned4(drow));
-  hipStream_t st = (hipStream_t)stream;
-  LH_TRY(launch_dos_prep(g, dos, os, (bf16_t *)dos_hi, (bf16_t *)dos_lo, drow, st));
-  LH_TRY(launch_transpose(g, dos_hi, dost_hi, st));
-  return launch_transpose(g, dos_lo, dost_lo, st);
+         aligned4(drow));
+  return launch_dos_prep(g, dos, os, (bf16_t *)dos_hi, (bf16_t *)dos_lo, drow,
+                         (hipStream_t)stream);
 }
 
 lh_status lh_attn_fwd_mfma(const lh_dims *dims, const void *qs, const void *ks, const void *vst,
@@ -327,40 +314,34 @@ lh_status lh_attn_fwd_mfma(const lh_dims *dims, const void *qs, const void *ks, 
 }
 
 lh_status lh_attn_bwd_dkv_mfma(const lh_dims *dims, const void *qs, const void *ks,
-                               const void *vs, const void *qst, const void *dos_hi,
-                               const void *dos_lo, const void *dost_hi, const void *dost_lo,
+                               const void *vs, const void *dos_hi, const void *dos_lo,
                                const float *lse, const float *drow, const uint8_t *sel_flags,
                                float *dks, float *dvs, lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
   if (g.io != LH_BF16) return LH_ERR_UNSUPPORTED;
-  LH_REQ(qs && ks && vs && qst && dos_hi && dos_lo && dost_hi && dost_lo && lse && drow &&
-         sel_flags && dks && dvs);
-  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(qst) &&
-         aligned16(dos_hi) && aligned16(dos_lo) && aligned16(dost_hi) && aligned16(dost_lo) &&
-         aligned4(lse) && aligned4(drow) && aligned16(dks) && aligned16(dvs));
+  LH_REQ(qs && ks && vs && dos_hi && dos_lo && lse && drow && sel_flags && dks && dvs);
+  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(dos_hi) &&
+         aligned16(dos_lo) && aligned4(lse) && aligned4(drow) && aligned16(dks) &&
+         aligned16(dvs));
   return launch_attn_bwd_dkv_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
-                                  (const bf16_t *)qst, (const bf16_t *)dos_hi,
-                                  (const bf16_t *)dos_lo, (const bf16_t *)dost_hi,
-                                  (const bf16_t *)dost_lo, lse, drow, sel_flags, dks, dvs,
-                                  (hipStream_t)stream);
+                                  (const bf16_t *)dos_hi, (const bf16_t *)dos_lo, lse, drow,
+                                  sel_flags, dks, dvs, (hipStream_t)stream);
 }
 
 lh_status lh_attn_bwd_dq_mfma(const lh_dims *dims, const void *qs, const void *ks,
-                              const void *vs, const void *kst, const void *dos_hi,
-                              const void *dos_lo, const float *lse, const float *drow,
-                              const uint8_t *sel_flags, float *dqs, lh_stream stream) {
+                              const void *vs, const void *dos_hi, const void *dos_lo,
+                              const float *lse, const float *drow, const uint8_t *sel_flags,
+                              float *dqs, lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
   if (g.io != LH_BF16) return LH_ERR_UNSUPPORTED;
-  LH_REQ(qs && ks && vs && kst && dos_hi && dos_lo && lse && drow && sel_flags && dqs);
-  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(kst) &&
-         aligned16(dos_hi) && aligned16(dos_lo) && aligned4(lse) && aligned4(drow) &&
-         aligned16(dqs));
+  LH_REQ(qs && ks && vs && dos_hi && dos_lo && lse && drow && sel_flags && dqs);
+  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(dos_hi) &&
+         aligned16(dos_lo) && aligned4(lse) && aligned4(drow) && aligned16(dqs));
   return launch_attn_bwd_dq_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
-                                 (const bf16_t *)kst, (const bf16_t *)dos_hi,
-                                 (const bf16_t *)dos_lo, lse, drow, sel_flags, dqs,
-                                 (hipStream_t)stream);
+                                 (const bf16_t *)dos_hi, (const bf16_t *)dos_lo, lse, drow,
+                                 sel_flags, dqs, (hipStream_t)stream);
 }
 
 lh_status lh_scatter(const lh_dims *dims, const void *os, const int32_t *sel_anchor,
@@ -404,10 +385,7 @@ static lh_status check_saved(const Geo &g, const lh_saved *s) {
          aligned4(s->sk) && aligned4(s->sel_idx) && aligned4(s->sel_anchor) &&
          aligned4(s->row_of) && aligned16(s->qs) && aligned16(s->ks) && aligned16(s->vs) &&
          aligned16(s->os) && aligned4(s->lse));
-  if (g.io == LH_BF16) {
-    LH_REQ(s->qst && s->kst && s->vst);
-    LH_REQ(aligned16(s->qst) && aligned16(s->kst) && aligned16(s->vst));
-  }
+  if (g.io == LH_BF16) LH_REQ(s->vst && aligned16(s->vst));
   return LH_OK;
 }
 
@@ -425,8 +403,8 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
   LH_TRY(launch_pyramid_score(g, q, k, v, s->pq, s->pk, s->pv, s->sq, s->sk, st));
   LH_TRY(launch_select(g, s->sq, s->sk, s->sel_idx, s->sel_anchor, s->sel_flags, s->row_of, st));
   const bool bf = g.io == LH_BF16;
-  LH_TRY(gather_impl(g, q, k, v, s->pq, s->pk, s->pv, s->sel_idx, s->qs, s->ks, s->vs,
-                     bf ? s->qst : nullptr, bf ? s->kst : nullptr, bf ? s->vst : nullptr, st));
+  LH_TRY(gather_impl(g, q, k, v, s->pq, s->pk, s->pv, s->sel_idx, s->qs, s->ks, s->vs, nullptr,
+                     nullptr, bf ? s->vst : nullptr, st));
   if (bf)
     LH_TRY(launch_attn_fwd_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
                                 (const bf16_t *)s->vst, s->sel_flags, (float *)s->os, s->lse,
@@ -456,17 +434,12 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
   if (g.io == LH_BF16) {
     bf16_t *dhi = (bf16_t *)c.take(rows_bf16(g));
     bf16_t *dlo = (bf16_t *)c.take(rows_bf16(g));
-    bf16_t *dthi = (bf16_t *)c.take(z.subseq_t);
-    bf16_t *dtlo = (bf16_t *)c.take(z.subseq_t);
     if (!c.ok()) return LH_ERR_WORKSPACE;
-    LH_TRY(launch_scatter_bwd(g, dout, s->sel_anchor, s->sel_flags, nullptr, dhi, dlo, (const float *)s->os,
-                              drow, st));
-    LH_TRY(launch_transpose(g, dhi, dthi, st));
-    LH_TRY(launch_transpose(g, dlo, dtlo, st));
+    LH_TRY(launch_scatter_bwd(g, dout, s->sel_anchor, s->sel_flags, nullptr, dhi, dlo,
+                              (const float *)s->os, drow, st));
     LH_TRY(launch_attn_bwd_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
-                                (const bf16_t *)s->vs, (const bf16_t *)s->qst,
-                                (const bf16_t *)s->kst, dhi, dlo, dthi, dtlo, s->lse, drow,
-                                s->sel_flags, dqs, dks, dvs, st));
+                                (const bf16_t *)s->vs, dhi, dlo, s->lse, drow, s->sel_flags, dqs,
+                                dks, dvs, st));
   } else {
     float *dos = (float *)c.take(z.subseq_f32);
     if (!c.ok()) return LH_ERR_WORKSPACE;

@@ -37,8 +37,6 @@ constexpr int kFwdBM = 128;   // queries per workgroup
 constexpr int kFwdBN = 64;    // keys per block
 constexpr int kFwdThreads = 512;
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 template <int D>
 struct FwdSmem {
   bf16_t k[2][2][kFwdBN * D];   // [group][buffer] key rows, swizzled 16-byte chunks

@@ -133,26 +133,23 @@ lh_status launch_attn_bwd_f32(const Geo &g, const float *qs, const float *ks, co
                               const float *dos, float *drow_ws, float *dqs, float *dks,
                               float *dvs, hipStream_t st);
 
-// attention, bf16 I/O (MFMA).  vst/qst/kst/dost_*: transposed [BH, d, Sp].
-// dO enters the backward as a two-term bf16 split (hi + lo).
+// attention, bf16 I/O (MFMA).  vst: transposed V [BH, d, Sp].  dO enters the
+// backward as a two-term bf16 split (hi + lo).
 lh_status launch_attn_fwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                const bf16_t *vst, const uint8_t *flags, float *os, float *lse,
                                hipStream_t st);
 lh_status launch_attn_bwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
-                               const bf16_t *vs, const bf16_t *qst, const bf16_t *kst,
-                               const bf16_t *dos_hi, const bf16_t *dos_lo,
-                               const bf16_t *dost_hi, const bf16_t *dost_lo, const float *lse,
-                               const float *drow, const uint8_t *flags, float *dqs,
-                               float *dks, float *dvs, hipStream_t st);
+                               const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
+                               const float *lse, const float *drow, const uint8_t *flags,
+                               float *dqs, float *dks, float *dvs, hipStream_t st);
 lh_status launch_attn_bwd_dkv_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
-                                   const bf16_t *vs, const bf16_t *qst, const bf16_t *dos_hi,
-                                   const bf16_t *dos_lo, const bf16_t *dost_hi,
-                                   const bf16_t *dost_lo, const float *lse, const float *drow,
-                                   const uint8_t *flags, float *dks, float *dvs, hipStream_t st);
+                                   const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
+                                   const float *lse, const float *drow, const uint8_t *flags,
+                                   float *dks, float *dvs, hipStream_t st);
 lh_status launch_attn_bwd_dq_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
-                                  const bf16_t *vs, const bf16_t *kst, const bf16_t *dos_hi,
-                                  const bf16_t *dos_lo, const float *lse, const float *drow,
-                                  const uint8_t *flags, float *dqs, hipStream_t st);
+                                  const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
+                                  const float *lse, const float *drow, const uint8_t *flags,
+                                  float *dqs, hipStream_t st);
 // float32 dos [BH,S,d] -> optional bf16 split (hi, lo) and drow = rowsum(dos * os)
 lh_status launch_dos_prep(const Geo &g, const float *dos, const float *os, bf16_t *dos_hi,
                           bf16_t *dos_lo, float *drow, hipStream_t st);

@@ -60,4 +60,67 @@ __device__ __forceinline__ void pack_split(const f32x16 &acc, int o, bf16x8 &hi,
   }
 }
 
+// ---------------------------------------------------------------- row tiles
+// A row tile X[r][n] (16-bit, D columns) in LDS is read two ways: as the
+// "row" operand (lane % 32 = row r, k = columns 16s + 8h .. +7) and as the
+// "column" operand (lane % 32 = column n, k = rows) with ds_read_b64_tr_b16.
+// The transposing read hands lane 4a+b of each 16-lane group element b of
+// the 8-byte pieces addressed by lanes a, a+4, a+8, a+12 of that group, so a
+// group whose lane j points at row kbase + j/4, columns n0 + 4(j%4) receives
+// column n0 + i of rows kbase..kbase+3 in its lane i.  16-byte chunks are
+// XOR-swizzled per row so that both reads stay free of bank conflicts.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+template <int D>
+__device__ __forceinline__ int swz_r(int r) {
+  int f = ((r & 3) << 1) | ((r >> 2) & 1);
+  if (D == 128) f |= ((r >> 3) & 1) << 3;
+  return f;
+}
+// element offset of (row r, column n) in a swizzled row tile
+template <int D>
+__device__ __forceinline__ int toff(int r, int n) {
+  return r * D + ((((n >> 3) ^ swz_r<D>(r))) << 3) + (n & 7);
+}
+// row operand: row r, k-step s (columns 16s + 8h .. +7)
+template <int D>
+__device__ __forceinline__ bf16x8 ld_rowop(const bf16_t *X, int r, int s, int h) {
+  return ld_bf16x8(X + toff<D>(r, 16 * s + 8 * h));
+}
+// column operand over the 32 columns nb .. nb+31, k-step s over rows, with
+// k-slot 8h + 4u + J <-> row 16s + 8u + 4h + J (the order pack_split uses for
+// an accumulator tile whose rows are 8I + 4h + J)
+template <int D>
+__device__ __forceinline__ bf16x8 ld_colop(const bf16_t *X, int s, int nb, int lane) {
+  const int j = lane & 15, g = lane >> 4, h = lane >> 5;
+  const int n = nb + 16 * (g & 1) + 4 * (j & 3);
+  const int r = 16 * s + 4 * h + (j >> 2);
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16 *)(X + toff<D>(r, n)));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16 *)(X + toff<D>(r + 8, n)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
+// async global -> LDS copy of `rows` rows of a [*, D] bf16 matrix (row stride
+// D) into a swizzled row tile, by the `nthr` threads t = 0..nthr-1 (whole
+// wavefronts); rows past `rmax` repeat row rmax
+template <int D>
+__device__ __forceinline__ void tile_load(bf16_t *dst, const bf16_t *src, int64_t row0,
+                                          int64_t rmax, int rows, int t, int nthr) {
+  const int lane = t & 63, w = t >> 6;
+  const int pieces = rows * D / 8 / 64;   // 1 KB pieces
+  for (int j = w; j < pieces; j += nthr / 64) {
+    const int chunk = j * 64 + lane;
+    const int r = chunk / (D / 8), p = chunk % (D / 8);
+    const int c = p ^ swz_r<D>(r);
+    const int64_t row = min(row0 + r, rmax);
+    __builtin_amdgcn_global_load_lds((const void *)(src + row * D + c * 8),
+                                     (lds_void *)(reinterpret_cast<unsigned char *>(dst) + j * 1024),
+                                     16, 0, 0);
+  }
+}
+
 }  // namespace lh

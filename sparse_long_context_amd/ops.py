@@ -149,14 +149,13 @@ def subseq_attn_bwd(c: Ctx, qs, ks, vs, os_, lse, flags, dos):
 
 
 def attn_bwd_prep(c: Ctx, dos, os_):
-    """Operands of the two backward MFMA kernels (bf16 I/O only)."""
+    """Operands of the two backward MFMA kernels (bf16 I/O only): the
+    two-term bf16 split of dOS and drow = rowsum(dOS * OS)."""
     dev = dos.device
     hi, lo = (c.empty(*_bh(c), c.S, c.d, dtype=torch.bfloat16, device=dev) for _ in range(2))
-    thi, tlo = (c.empty(*_bh(c), c.d, c.Sp, dtype=torch.bfloat16, device=dev) for _ in range(2))
     drow = c.empty(*_bh(c), c.S, dtype=torch.float32, device=dev)
-    c.call("lh_attn_bwd_prep", _ptr(dos), _ptr(os_), _ptr(hi), _ptr(lo), _ptr(thi), _ptr(tlo),
-           _ptr(drow), _stream())
-    return hi, lo, thi, tlo, drow
+    c.call("lh_attn_bwd_prep", _ptr(dos), _ptr(os_), _ptr(hi), _ptr(lo), _ptr(drow), _stream())
+    return hi, lo, drow
 
 
 def attn_fwd_mfma(c: Ctx, qs, ks, vst, flags, os_=None, lse=None):
@@ -168,22 +167,20 @@ def attn_fwd_mfma(c: Ctx, qs, ks, vst, flags, os_=None, lse=None):
     return os_, lse
 
 
-def attn_bwd_dkv_mfma(c: Ctx, qs, ks, vs, qst, hi, lo, thi, tlo, lse, drow, flags, dks=None,
-                      dvs=None):
+def attn_bwd_dkv_mfma(c: Ctx, qs, ks, vs, hi, lo, lse, drow, flags, dks=None, dvs=None):
     dev = qs.device
     dks = c.empty(*_bh(c), c.S, c.d, dtype=torch.float32, device=dev) if dks is None else dks
     dvs = c.empty(*_bh(c), c.S, c.d, dtype=torch.float32, device=dev) if dvs is None else dvs
-    c.call("lh_attn_bwd_dkv_mfma", _ptr(qs), _ptr(ks), _ptr(vs), _ptr(qst), _ptr(hi), _ptr(lo),
-           _ptr(thi), _ptr(tlo), _ptr(lse), _ptr(drow), _ptr(flags), _ptr(dks), _ptr(dvs),
-           _stream())
+    c.call("lh_attn_bwd_dkv_mfma", _ptr(qs), _ptr(ks), _ptr(vs), _ptr(hi), _ptr(lo), _ptr(lse),
+           _ptr(drow), _ptr(flags), _ptr(dks), _ptr(dvs), _stream())
     return dks, dvs
 
 
-def attn_bwd_dq_mfma(c: Ctx, qs, ks, vs, kst, hi, lo, lse, drow, flags, dqs=None):
+def attn_bwd_dq_mfma(c: Ctx, qs, ks, vs, hi, lo, lse, drow, flags, dqs=None):
     dev = qs.device
     dqs = c.empty(*_bh(c), c.S, c.d, dtype=torch.float32, device=dev) if dqs is None else dqs
-    c.call("lh_attn_bwd_dq_mfma", _ptr(qs), _ptr(ks), _ptr(vs), _ptr(kst), _ptr(hi), _ptr(lo),
-           _ptr(lse), _ptr(drow), _ptr(flags), _ptr(dqs), _stream())
+    c.call("lh_attn_bwd_dq_mfma", _ptr(qs), _ptr(ks), _ptr(vs), _ptr(hi), _ptr(lo), _ptr(lse),
+           _ptr(drow), _ptr(flags), _ptr(dqs), _stream())
     return dqs
 
 
@@ -233,8 +230,7 @@ def alloc_saved(c: Ctx, device):
     for n in ("qs", "ks", "vs"):
         s[n] = torch.empty(*bh, c.S, c.d, dtype=c.io, device=device)
     if c.io == torch.bfloat16:
-        for n in ("qst", "kst", "vst"):
-            s[n] = torch.empty(*bh, c.d, c.Sp, dtype=c.io, device=device)
+        s["vst"] = torch.empty(*bh, c.d, c.Sp, dtype=c.io, device=device)
     return s
 
 
