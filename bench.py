@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=10)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known byte "
+                         "count that calibrates hardware traffic counters)")
     return ap.parse_args()
 
 
@@ -140,6 +143,15 @@ def main():
     def step():
         ops.layer_fwd(c, Q, K, V, saved=saved, o=o)
         ops.layer_bwd(c, saved, dO, ws=ws, outs=grads)
+
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src, dst = torch.ones(n, device=dev), torch.empty(n, device=dev)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {args.copy_mib} MiB (read {args.copy_mib} MiB, write "
+              f"{args.copy_mib} MiB)", file=sys.stderr, flush=True)
+        del src, dst
 
     for _ in range(args.warmup):
         step()

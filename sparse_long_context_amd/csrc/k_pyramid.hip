@@ -36,9 +36,10 @@ struct PyrArgs {
   int64_t lsize[kMaxLevels], loff[kMaxLevels], pw[kMaxLevels + 1];
 };
 
-template <typename T, int CPR>
+template <typename T, int CPR, int G>
 __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
   extern __shared__ float lds[];                 // [spw*R][d] sums, then [spw*R] maxima
+  constexpr int U = 8;                           // token rows in flight per thread
   const int z = blockIdx.z;
   const T *X = (const T *)a.in[z];
   if (!X) return;
@@ -54,29 +55,30 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
   const int rs = tid / CPR;                // row slot in workgroup
   const int sub = rs / a.R, r = rs % a.R;  // stratum within workgroup, subtree
   const int64_t m = (int64_t)blockIdx.x * a.spw + sub;
-  const int G = (int)a.pw[a.g];
-  const int64_t base = m * a.Bc + (int64_t)r * G;
+  const int Gt = (int)a.pw[G];             // tokens of the subtree
+  const int64_t base = m * a.Bc + (int64_t)r * Gt;
   const int rows = a.spw * a.R;
   float *lsum = lds;                       // [rows][d]
   float *lmax = lds + (size_t)rows * d;    // [rows]
 
-  float acc[kPyrMaxG + 2][8];
-  float smx[kPyrMaxG + 2];
+  // running sums / maxima of the levels 1..G entries being completed
+  float acc[G + 1][8];
+  float smx[G + 1];
 #pragma unroll
-  for (int l = 0; l <= kPyrMaxG + 1; ++l) {
+  for (int l = 0; l <= G; ++l) {
     smx[l] = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[l][i] = 0.f;
   }
 
-  for (int t0 = 0; t0 < G; t0 += 4) {
-    float x[4][8];
+  for (int t0 = 0; t0 < Gt; t0 += U) {
+    float x[U][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (t0 + u < G) load8(X + (base + t0 + u) * d + c * 8, x[u]);
+    for (int u = 0; u < U; ++u)
+      if (t0 + u < Gt) load8(X + (base + t0 + u) * d + c * 8, x[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (t0 + u >= G) break;
+    for (int u = 0; u < U; ++u) {
+      if (t0 + u >= Gt) break;
       const int64_t tok = base + t0 + u;
       float s = 0.f;
       if (do_sc) {
@@ -88,50 +90,50 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
         s = (float)sqrt(ss);
         if (c == 0) Sc[tok] = s;
       }
-      if (a.g == 0) {
+      if constexpr (G == 0) {
         // the subtree is a single token: it goes straight to LDS
 #pragma unroll
         for (int i = 0; i < 8; ++i) lsum[(size_t)rs * d + c * 8 + i] = x[u][i];
         if (c == 0) lmax[rs] = s;
-        continue;
-      }
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[1][i] += x[u][i];
-      smx[1] = fmaxf(smx[1], s);
-      const int64_t cnt = t0 + u + 1;
+        for (int i = 0; i < 8; ++i) acc[1][i] += x[u][i];
+        smx[1] = fmaxf(smx[1], s);
+        const int cnt = t0 + u + 1;
 #pragma unroll
-      for (int l = 1; l <= kPyrMaxG; ++l) {
-        if (l > a.g || cnt % a.pw[l] != 0) break;
-        const int64_t idx = (tok + 1) / a.pw[l] - 1;   // index within level l
-        if (do_pyr) {
-          const float inv = (float)a.pw[l];
-          float mean[8];
+        for (int l = 1; l <= G; ++l) {
+          if (cnt % (int)a.pw[l] != 0) break;
+          const int64_t idx = (tok + 1) / a.pw[l] - 1;   // index within level l
+          if (do_pyr) {
+            const float inv = (float)a.pw[l];
+            float mean[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) mean[i] = acc[l][i] / inv;
-          store8(P + (a.loff[l] - a.N + idx) * d + c * 8, mean);
+            for (int i = 0; i < 8; ++i) mean[i] = acc[l][i] / inv;
+            store8(P + (a.loff[l] - a.N + idx) * d + c * 8, mean);
+          }
+          if (do_sc && c == 0) Sc[a.loff[l] + idx] = smx[l];
+          if (l == G) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) lsum[(size_t)rs * d + c * 8 + i] = acc[l][i];
+            if (c == 0) lmax[rs] = smx[l];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[l + 1][i] += acc[l][i];
+            smx[l + 1] = fmaxf(smx[l + 1], smx[l]);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[l][i] = 0.f;
+          smx[l] = 0.f;
         }
-        if (do_sc && c == 0) Sc[a.loff[l] + idx] = smx[l];
-        if (l == a.g) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) lsum[(size_t)rs * d + c * 8 + i] = acc[l][i];
-          if (c == 0) lmax[rs] = smx[l];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[l + 1][i] += acc[l][i];
-          smx[l + 1] = fmaxf(smx[l + 1], smx[l]);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[l][i] = 0.f;
-        smx[l] = 0.f;
       }
     }
   }
   __syncthreads();
 
-  // levels g+1 .. L-1 of each stratum from the LDS sums (compacted in place:
+  // levels G+1 .. L-1 of each stratum from the LDS sums (compacted in place:
   // entry e of the current level lives in row sub*R + e)
   int n = a.R;
-  for (int l = a.g + 1; l < a.L; ++l) {
+  for (int l = G + 1; l < a.L; ++l) {
     n /= a.p;
     const bool act = rs < a.spw * n;
     const int s2 = act ? rs / n : 0, e = act ? rs % n : 0;
@@ -212,13 +214,21 @@ lh_status launch_pyramid_score(const Geo &g, const void *q, const void *k, const
   dim3 grid((unsigned)(g.n_c / a.spw), (unsigned)g.BH(), (unsigned)nz);
   dim3 block((unsigned)(a.spw * a.R * cpr));
   const size_t shm = (size_t)a.spw * a.R * (g.d + 1) * sizeof(float);
-  if (g.io == LH_BF16) {
-    if (g.d == 128) hipLaunchKernelGGL((pyr_score_kernel<bf16_t, 16>), grid, block, shm, st, a);
-    else hipLaunchKernelGGL((pyr_score_kernel<bf16_t, 8>), grid, block, shm, st, a);
-  } else {
-    if (g.d == 128) hipLaunchKernelGGL((pyr_score_kernel<float, 16>), grid, block, shm, st, a);
-    else hipLaunchKernelGGL((pyr_score_kernel<float, 8>), grid, block, shm, st, a);
+#define LH_PYR_G(T, C, GG) \
+  case GG: hipLaunchKernelGGL((pyr_score_kernel<T, C, GG>), grid, block, shm, st, a); break;
+#define LH_PYR(T, C)                                                                          \
+  switch (a.g) {                                                                              \
+    LH_PYR_G(T, C, 0) LH_PYR_G(T, C, 1) LH_PYR_G(T, C, 2) LH_PYR_G(T, C, 3)                   \
+    LH_PYR_G(T, C, 4) LH_PYR_G(T, C, 5) LH_PYR_G(T, C, 6)                                     \
+    default: return LH_ERR_UNSUPPORTED;                                                       \
   }
+  if (g.io == LH_BF16) {
+    if (g.d == 128) { LH_PYR(bf16_t, 16) } else { LH_PYR(bf16_t, 8) }
+  } else {
+    if (g.d == 128) { LH_PYR(float, 16) } else { LH_PYR(float, 8) }
+  }
+#undef LH_PYR
+#undef LH_PYR_G
   return hip_status();
 }
 

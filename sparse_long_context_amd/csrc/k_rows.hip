@@ -162,22 +162,29 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatArgs a) {
   const int d = a.d;
   const float *os = a.os + bh * a.S * d;
   T *o = (T *)a.o + bh * a.N * d;
-  for (int64_t t = t_begin + threadIdx.x / CPR; t < t_end; t += 256 / CPR) {
-    // last row with anchor <= t
-    int lo = 0, hi = nr;          // answer in [lo-1, hi-1]
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (sanc[mid] <= t) lo = mid + 1; else hi = mid;
-    }
-    const int32_t src = lo == 0 ? prev_leader : lead[lo - 1];
-    float x[8];
-    if (src >= 0 && src < a.S) {
-      load8(os + (int64_t)src * d + c * 8, x);
-    } else {
+  constexpr int TW = 256 / CPR;   // token lanes
+  for (int64_t tb = t_begin + threadIdx.x / CPR; tb < t_end; tb += 4 * TW) {
+    float x[4][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    for (int k = 0; k < 4; ++k) {
+      const int64_t t = tb + k * TW;
+      // last row with anchor <= t
+      int lo = 0, hi = nr;          // answer in [lo-1, hi-1]
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sanc[mid] <= t) lo = mid + 1; else hi = mid;
+      }
+      const int32_t src = lo == 0 ? prev_leader : lead[lo - 1];
+      if (t < t_end && src >= 0 && src < a.S) {
+        load8(os + (int64_t)src * d + c * 8, x[k]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[k][i] = 0.f;
+      }
     }
-    store8(o + t * d + c * 8, x);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (tb + k * TW < t_end) store8(o + (tb + k * TW) * d + c * 8, x[k]);
   }
 }
 
@@ -237,11 +244,18 @@ __global__ __launch_bounds__(256) void scatter_bwd_kernel(ScatBwdArgs a) {
     while (nx < a.S && anc[nx] == anc[j]) ++nx;
     const int64_t t1 = max(t0, min(nx < a.S ? (int64_t)anc[nx] : a.N, a.N));
     const T *dO = (const T *)a.dout + bh * a.N * d;
-    for (int64_t t = t0 + u; t < t1; t += TL) {
-      float x[8];
-      load8(dO + t * d + c * 8, x);
+    // four rows in flight per lane; each lane still adds its tokens in order
+    for (int64_t t = t0 + u; t < t1; t += 4 * TL) {
+      float x[4][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += x[i];
+      for (int k = 0; k < 4; ++k)
+        if (t + k * TL < t1) load8(dO + (t + k * TL) * d + c * 8, x[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (t + k * TL < t1) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += x[k][i];
+        }
     }
 #pragma unroll
     for (int off = CPR; off < 64; off <<= 1)
@@ -322,61 +336,131 @@ lh_status launch_dos_prep(const Geo &g, const float *dos, const float *os, bf16_
 
 // ---------------------------------------------------------------- unpool
 // dx[t] = sum_l dxs[row_of(l, t / p^l)] / p^l over the selected ancestors of
-// t, in level order.  CPR lanes per token row.
+// t.  One workgroup covers `spw` whole strata of one (b, h) and one tensor:
+// the strata's row_of entries (their subtrees) are staged in LDS, so lookups
+// are LDS reads.  A thread walks level-1 entries (CPR lanes per row): the
+// levels L-1..1 part, shared by the entry's p tokens, is summed once
+// (coarsest first), then each token adds its own level-0 row when selected.
+// The summation order is fixed, so results are reproducible.
+constexpr int kUnpoolThreads = 256;
+constexpr int kUnpoolLdsEntries = 8192;   // row_of entries staged per workgroup
+
 struct UnpoolArgs {
   const float *dxs[3];
   void *dx[3];
   const int32_t *row_of;
-  int64_t N, E, S;
-  int32_t d, L;
+  int64_t N, E, S, Bc;
+  int32_t d, L, p, spw, lgp;    // lgp = log2(p) when p is a power of two, else -1
+  int32_t T;                 // subtree entries per stratum
   int64_t loff[kMaxLevels], pw[kMaxLevels];
+  int32_t cstart[kMaxLevels];   // first entry of level l inside a stratum's subtree
   float inv[kMaxLevels];
 };
 
 template <typename TO, int CPR>
-__global__ __launch_bounds__(256) void unpool_kernel(UnpoolArgs a) {
+__global__ __launch_bounds__(kUnpoolThreads) void unpool_kernel(UnpoolArgs a) {
+  __shared__ int32_t ro[kUnpoolLdsEntries];
   const int z = blockIdx.z;
   const int64_t bh = blockIdx.y;
-  const int64_t t = (int64_t)blockIdx.x * (256 / CPR) + threadIdx.x / CPR;
-  if (t >= a.N) return;
-  const int c = threadIdx.x % CPR;
+  const int64_t m0 = (int64_t)blockIdx.x * a.spw;   // first stratum of the workgroup
+  const int tid = threadIdx.x;
+  const int32_t *rog = a.row_of + bh * a.E;
+  // stage row_of of the spw subtrees: entry (s, l, j) at s*T + cstart[l] + j
+  for (int i = tid; i < a.spw * a.T; i += kUnpoolThreads) {
+    const int sidx = i / a.T, e = i % a.T;
+    int l = 0;
+    while (l + 1 < a.L && e >= a.cstart[l + 1]) ++l;
+    const int64_t per = a.Bc / a.pw[l];
+    const int32_t r = rog[a.loff[l] + (m0 + sidx) * per + (e - a.cstart[l])];
+    ro[i] = (r >= 0 && r < a.S) ? r : -1;
+  }
+  __syncthreads();
+  const int c = tid % CPR;
+  constexpr int LANES = kUnpoolThreads / CPR;   // lanes along the tokens
   const int d = a.d;
-  const int32_t *ro = a.row_of + bh * a.E;
   const float *dxs = a.dxs[z] + bh * a.S * d;
-  float acc[8];
+  TO *out = (TO *)a.dx[z] + bh * a.N * d;
+  const int64_t t0 = m0 * a.Bc;
+  const int ntok = a.spw * (int)a.Bc;
+  // work unit: one level-1 entry (p tokens; a single token when L == 1),
+  // whose tokens share every ancestor above level 0
+  const int P1 = a.L >= 2 ? a.p : 1;
+  const int nent = ntok / P1;
+  const int per = (nent + LANES - 1) / LANES;
+  const int e_begin = (tid / CPR) * per, e_end = min(nent, e_begin + per);
+  for (int e = e_begin; e < e_end; ++e) {
+    const int u0 = e * P1;
+    const int sidx = u0 / (int)a.Bc, ul = u0 - sidx * (int)a.Bc;
+    const int base = sidx * a.T;
+    // coarse part: levels L-1 .. 1, coarsest first
+    float A[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int l = 0; l < a.L; ++l) {
-    const int32_t r = ro[a.loff[l] + t / a.pw[l]];
-    if (r >= 0 && r < a.S) {
-      float x[8];
-      load8(dxs + (int64_t)r * d + c * 8, x);
-      const float w = a.inv[l];
+    for (int i = 0; i < 8; ++i) A[i] = 0.f;
+    for (int l = a.L - 1; l >= 1; --l) {
+      const int j = a.lgp >= 0 ? (ul >> (a.lgp * l)) : (int)(ul / a.pw[l]);
+      const int32_t r = ro[base + a.cstart[l] + j];
+      if (r >= 0) {
+        float x[8];
+        load8(dxs + (int64_t)r * d + c * 8, x);
+        const float w = a.inv[l];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += x[i] * w;
+        for (int i = 0; i < 8; ++i) A[i] += x[i] * w;
+      }
+    }
+    // the entry's tokens: A plus their own level-0 row when selected
+    for (int k0 = 0; k0 < P1; k0 += 4) {
+      float x[4][8];
+      int32_t r[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        r[k] = k0 + k < P1 ? ro[base + ul + k0 + k] : -1;   // level 0 starts at entry 0
+        if (r[k] >= 0) load8(dxs + (int64_t)r[k] * d + c * 8, x[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (k0 + k >= P1) break;
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = r[k] >= 0 ? A[i] + x[k][i] : A[i];
+        store8(out + (t0 + u0 + k0 + k) * d + c * 8, o);
+      }
     }
   }
-  store8((TO *)a.dx[z] + (bh * a.N + t) * d + c * 8, acc);
+}
+
+static int unpool_spw(const Geo &g) {
+  int spw = (int)(1024 / g.Bc);
+  if (spw < 1) spw = 1;
+  while (spw > 1 && (spw * g.T > kUnpoolLdsEntries || g.n_c % spw)) --spw;
+  return spw;
 }
 
 lh_status launch_unpool(const Geo &g, const float *const dxs[3], const int32_t *row_of,
                         void *const dx[3], hipStream_t st) {
+  if (g.T > kUnpoolLdsEntries) return LH_ERR_UNSUPPORTED;
   UnpoolArgs a;
   for (int i = 0; i < 3; ++i) { a.dxs[i] = dxs[i]; a.dx[i] = dx[i]; }
-  a.row_of = row_of; a.N = g.N; a.E = g.E; a.S = g.S; a.d = g.d; a.L = g.L;
+  a.row_of = row_of; a.N = g.N; a.E = g.E; a.S = g.S; a.Bc = g.Bc; a.d = g.d; a.L = g.L;
+  a.p = g.p; a.T = (int32_t)g.T;
+  a.spw = unpool_spw(g);
+  a.lgp = -1;
+  for (int k = 0; k < 31; ++k)
+    if ((1 << k) == g.p) a.lgp = k;
+  int cs = 0;
   for (int l = 0; l < kMaxLevels; ++l) {
     a.loff[l] = g.loff[l];
     a.pw[l] = g.pw[l];
     a.inv[l] = (float)(1.0 / (double)g.pw[l]);
+    a.cstart[l] = cs;
+    if (l < g.L) cs += (int)(g.Bc / g.pw[l]);
   }
-  const int cpr = g.d / 8;
-  dim3 grid(cdiv(g.N, 256 / cpr), (unsigned)g.BH(), 3);
+  dim3 grid((unsigned)(g.n_c / a.spw), (unsigned)g.BH(), 3);
   if (g.out == LH_BF16) {
-    if (g.d == 128) hipLaunchKernelGGL((unpool_kernel<bf16_t, 16>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((unpool_kernel<bf16_t, 8>), grid, dim3(256), 0, st, a);
+    if (g.d == 128) hipLaunchKernelGGL((unpool_kernel<bf16_t, 16>), grid, dim3(kUnpoolThreads), 0, st, a);
+    else hipLaunchKernelGGL((unpool_kernel<bf16_t, 8>), grid, dim3(kUnpoolThreads), 0, st, a);
   } else {
-    if (g.d == 128) hipLaunchKernelGGL((unpool_kernel<float, 16>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((unpool_kernel<float, 8>), grid, dim3(256), 0, st, a);
+    if (g.d == 128) hipLaunchKernelGGL((unpool_kernel<float, 16>), grid, dim3(kUnpoolThreads), 0, st, a);
+    else hipLaunchKernelGGL((unpool_kernel<float, 8>), grid, dim3(kUnpoolThreads), 0, st, a);
   }
   return hip_status();
 }
