@@ -88,8 +88,13 @@ def counters_for(kernel: str, workload_name: str):
         return None
     if not rec or rec.get("workload") != workload_name:
         return None
-    src = os.path.join(ROOT, "sparse_long_context_amd", "csrc", rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sha256"]:
+    h = hashlib.sha256()
+    for name in rec["sources"]:
+        src = os.path.join(ROOT, "sparse_long_context_amd", "csrc", name)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if h.hexdigest() != rec["sha256"]:
         return None
     return rec.get("bytes_per_launch")
 

@@ -34,7 +34,51 @@ struct PyrArgs {
   int64_t N, E, Bc;
   int32_t d, p, L, g, R, spw;
   int64_t lsize[kMaxLevels], loff[kMaxLevels], pw[kMaxLevels + 1];
+  int64_t per[kMaxLevels];   // entries of level l per stratum (Bc / p^l)
+  float rp[kMaxLevels];      // 1 / p^l
 };
+
+// a float64 moved across lanes by one DPP pattern (both halves)
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+
+// sum over the CPR (8 or 16) lanes of a row group, left in every lane of the
+// group: swap neighbours, swap pairs, mirror halves of 8 (and halves of 16);
+// each step adds two equal-sized partial sums, so all lanes end bit-equal
+template <int CPR>
+__device__ __forceinline__ double rowsum_f64(double v) {
+  v += dpp_f64<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);   // row_half_mirror
+  if constexpr (CPR == 16) v += dpp_f64<0x140>(v);   // row_mirror
+  return v;
+}
+
+// lane u (or 8 + u) of each row group of CPR lanes, broadcast to the group
+template <int CPR>
+__device__ __forceinline__ float group_bcast(float v, int u) {
+  const int x = __float_as_int(v);
+  int r;
+  switch (u) {
+#define LH_BC(U)                                                                        \
+  case U:                                                                               \
+    if constexpr (CPR == 16) {                                                          \
+      r = __builtin_amdgcn_update_dpp(0, x, 0x150 + U, 0xf, 0xf, false);                \
+    } else {                                                                            \
+      r = __builtin_amdgcn_update_dpp(0, x, 0x150 + U, 0xf, 0x3, false);                \
+      r = __builtin_amdgcn_update_dpp(r, x, 0x158 + U, 0xf, 0xc, false);                \
+    }                                                                                   \
+    break;
+    LH_BC(0) LH_BC(1) LH_BC(2) LH_BC(3) LH_BC(4) LH_BC(5) LH_BC(6) LH_BC(7)
+#undef LH_BC
+    default: r = x;
+  }
+  return __int_as_float(r);
+}
 
 template <typename T, int CPR, int G>
 __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
@@ -61,12 +105,18 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
   float *lsum = lds;                       // [rows][d]
   float *lmax = lds + (size_t)rows * d;    // [rows]
 
-  // running sums / maxima of the levels 1..G entries being completed
+  // running sums / maxima of the levels 1..G entries being completed, the
+  // children each has taken so far, and the index (within its level) of the
+  // entry it will complete next
   float acc[G + 1][8];
   float smx[G + 1];
+  int cnt[G + 1];
+  int64_t idx[G + 1];
 #pragma unroll
   for (int l = 0; l <= G; ++l) {
     smx[l] = 0.f;
+    cnt[l] = 0;
+    idx[l] = m * a.per[l] + (int64_t)r * a.pw[G - l];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[l][i] = 0.f;
   }
@@ -74,22 +124,43 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
   for (int t0 = 0; t0 < Gt; t0 += U) {
     float x[U][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (t0 + u < Gt) load8(X + (base + t0 + u) * d + c * 8, x[u]);
+    for (int u = 0; u < U; ++u) {
+      if (t0 + u < Gt) {
+        load8(X + (base + t0 + u) * d + c * 8, x[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[u][i] = 0.f;
+      }
+    }
+    // l2 norms of the U rows: float64 sums of squares over the row group;
+    // lane c takes the square root of row c % U only, then every lane
+    // receives all U norms
+    float s_all[U];
+    if (do_sc) {
+      double ss[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        double t = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t += (double)x[u][i] * (double)x[u][i];
+        ss[u] = rowsum_f64<CPR>(t);
+      }
+      const int own = c & (U - 1);
+      double mine = ss[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mine = own == u ? ss[u] : mine;
+      const float s_own = (float)sqrt(mine);
+      if (c < U && t0 + c < Gt) Sc[base + t0 + c] = s_own;
+#pragma unroll
+      for (int u = 0; u < U; ++u) s_all[u] = group_bcast<CPR>(s_own, u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) s_all[u] = 0.f;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t0 + u >= Gt) break;
-      const int64_t tok = base + t0 + u;
-      float s = 0.f;
-      if (do_sc) {
-        double ss = 0.0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss += (double)x[u][i] * (double)x[u][i];
-#pragma unroll
-        for (int off = CPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-        s = (float)sqrt(ss);
-        if (c == 0) Sc[tok] = s;
-      }
+      const float s = s_all[u];
       if constexpr (G == 0) {
         // the subtree is a single token: it goes straight to LDS
 #pragma unroll
@@ -99,19 +170,18 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[1][i] += x[u][i];
         smx[1] = fmaxf(smx[1], s);
-        const int cnt = t0 + u + 1;
 #pragma unroll
         for (int l = 1; l <= G; ++l) {
-          if (cnt % (int)a.pw[l] != 0) break;
-          const int64_t idx = (tok + 1) / a.pw[l] - 1;   // index within level l
+          if (++cnt[l] < a.p) break;
+          cnt[l] = 0;
           if (do_pyr) {
-            const float inv = (float)a.pw[l];
             float mean[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) mean[i] = acc[l][i] / inv;
-            store8(P + (a.loff[l] - a.N + idx) * d + c * 8, mean);
+            for (int i = 0; i < 8; ++i) mean[i] = acc[l][i] * a.rp[l];
+            store8(P + (a.loff[l] - a.N + idx[l]) * d + c * 8, mean);
           }
-          if (do_sc && c == 0) Sc[a.loff[l] + idx] = smx[l];
+          if (do_sc && c == 0) Sc[a.loff[l] + idx[l]] = smx[l];
+          ++idx[l];
           if (l == G) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) lsum[(size_t)rs * d + c * 8 + i] = acc[l][i];
@@ -158,10 +228,9 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
       const int64_t mm = (int64_t)blockIdx.x * a.spw + s2;
       const int64_t idx = mm * n + e;
       if (do_pyr) {
-        const float inv = (float)a.pw[l];
         float mean[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) mean[i] = sum[i] / inv;
+        for (int i = 0; i < 8; ++i) mean[i] = sum[i] * a.rp[l];
         store8(P + (a.loff[l] - a.N + idx) * d + c * 8, mean);
       }
       if (do_sc && c == 0) Sc[a.loff[l] + idx] = mx;
@@ -206,6 +275,10 @@ lh_status launch_pyramid_score(const Geo &g, const void *q, const void *k, const
   a.N = g.N; a.E = g.E; a.Bc = g.Bc; a.d = g.d; a.p = g.p; a.L = g.L;
   for (int l = 0; l < kMaxLevels; ++l) { a.lsize[l] = g.lsize[l]; a.loff[l] = g.loff[l]; }
   for (int l = 0; l <= kMaxLevels; ++l) a.pw[l] = g.pw[l];
+  for (int l = 0; l < kMaxLevels; ++l) {
+    a.per[l] = l < g.L ? g.Bc / g.pw[l] : 0;
+    a.rp[l] = l < g.L ? (float)(1.0 / (double)g.pw[l]) : 0.f;
+  }
   if (!pyr_plan(g, &a.g, &a.R, &a.spw)) return LH_ERR_UNSUPPORTED;
   int nz = 0;
   for (int z = 0; z < 3; ++z) nz = a.in[z] ? z + 1 : nz;

@@ -112,11 +112,13 @@ lh_status launch_transpose(const Geo &g, const void *rows, void *tr, hipStream_t
 }
 
 // ---------------------------------------------------------------- scatter
-// One workgroup per (token chunk of one stratum, b*h).  The stratum's rows are
-// staged in LDS; each token finds its row by binary search on the anchors,
-// then its leader (first row at that anchor).  Tokens before the stratum's
-// first anchor take the last leader of the previous stratum.
-constexpr int kScatChunk = 1024;
+// One workgroup per (chunk of kScatChunk tokens of one stratum, b*h).  The
+// stratum's anchors are staged in LDS; each thread resolves one token's hold
+// source (the leader of the last row with anchor <= t, found by binary
+// search; tokens before the stratum's first anchor take the last leader of
+// the previous stratum) into an LDS map, then the workgroup streams the
+// source rows out, CPR lanes per row, NF rows in flight per lane.
+constexpr int kScatChunk = 256;
 
 struct ScatArgs {
   const float *os;
@@ -131,10 +133,11 @@ template <typename T, int CPR>
 __global__ __launch_bounds__(256) void scatter_kernel(ScatArgs a) {
   extern __shared__ int32_t sanc[];        // [k_s+1] anchors, then [k_s+1] leader rows
   __shared__ int32_t prev_leader;
+  __shared__ int32_t srcmap[kScatChunk];
   const int64_t bh = blockIdx.y;
   const int64_t m = blockIdx.x / a.chunks;
   const int64_t t_begin = m * a.Bc + (int64_t)(blockIdx.x % a.chunks) * kScatChunk;
-  const int64_t t_end = min(m * a.Bc + a.Bc, t_begin + kScatChunk);
+  const int ntok = (int)min((int64_t)kScatChunk, m * a.Bc + a.Bc - t_begin);
   const int nr = (int)(a.k_s + 1);
   const int64_t row0 = m * nr;
   const int32_t *anc = a.anchor + bh * a.S;
@@ -158,33 +161,39 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatArgs a) {
     lead[r] = (int32_t)(row0 + rr);
   }
   __syncthreads();
+  for (int i = threadIdx.x; i < ntok; i += 256) {
+    const int64_t t = t_begin + i;
+    int lo = 0, hi = nr;          // last row with anchor <= t is lo - 1
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sanc[mid] <= t) lo = mid + 1; else hi = mid;
+    }
+    const int32_t src = lo == 0 ? prev_leader : lead[lo - 1];
+    srcmap[i] = (src >= 0 && src < a.S) ? src : -1;
+  }
+  __syncthreads();
   const int c = threadIdx.x % CPR;
   const int d = a.d;
-  const float *os = a.os + bh * a.S * d;
-  T *o = (T *)a.o + bh * a.N * d;
+  const float *os = a.os + bh * a.S * d + c * 8;
+  T *o = (T *)a.o + (bh * a.N + t_begin) * d + c * 8;
   constexpr int TW = 256 / CPR;   // token lanes
-  for (int64_t tb = t_begin + threadIdx.x / CPR; tb < t_end; tb += 4 * TW) {
-    float x[4][8];
+  constexpr int NF = 8;
+  for (int tb = threadIdx.x / CPR; tb < ntok; tb += NF * TW) {
+    float x[NF][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t t = tb + k * TW;
-      // last row with anchor <= t
-      int lo = 0, hi = nr;          // answer in [lo-1, hi-1]
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sanc[mid] <= t) lo = mid + 1; else hi = mid;
-      }
-      const int32_t src = lo == 0 ? prev_leader : lead[lo - 1];
-      if (t < t_end && src >= 0 && src < a.S) {
-        load8(os + (int64_t)src * d + c * 8, x[k]);
+    for (int k = 0; k < NF; ++k) {
+      const int i = tb + k * TW;
+      const int32_t src = i < ntok ? srcmap[i] : -1;
+      if (src >= 0) {
+        load8(os + (int64_t)src * d, x[k]);
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[k][i] = 0.f;
+        for (int e = 0; e < 8; ++e) x[k][e] = 0.f;
       }
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (tb + k * TW < t_end) store8(o + (tb + k * TW) * d + c * 8, x[k]);
+    for (int k = 0; k < NF; ++k)
+      if (tb + k * TW < ntok) store8(o + (int64_t)(tb + k * TW) * d, x[k]);
   }
 }
 
@@ -212,6 +221,32 @@ lh_status launch_scatter(const Geo &g, const float *os, const int32_t *sel_ancho
 // in a fixed order.  Optionally writes the float32 sums, their two-term bf16
 // split (the MFMA operands of the attention backward) and
 // drow = <dOS_j, OS_j>.
+// 8 consecutive elements held as loaded (bf16 stays packed: 4 registers)
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  uint4 w;
+  __device__ void load(const bf16_t *p) { w = *reinterpret_cast<const uint4 *>(p); }
+  __device__ void add_to(float *acc) const {
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += __uint_as_float(v[i] << 16);
+      acc[2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ void load(const float *p) {
+    a = *reinterpret_cast<const float4 *>(p);
+    b = *reinterpret_cast<const float4 *>(p + 4);
+  }
+  __device__ void add_to(float *acc) const {
+    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
+};
+
 struct ScatBwdArgs {
   const void *dout;
   const int32_t *anchor;
@@ -243,19 +278,18 @@ __global__ __launch_bounds__(256) void scatter_bwd_kernel(ScatBwdArgs a) {
     int64_t nx = j + 1;
     while (nx < a.S && anc[nx] == anc[j]) ++nx;
     const int64_t t1 = max(t0, min(nx < a.S ? (int64_t)anc[nx] : a.N, a.N));
-    const T *dO = (const T *)a.dout + bh * a.N * d;
-    // four rows in flight per lane; each lane still adds its tokens in order
-    for (int64_t t = t0 + u; t < t1; t += 4 * TL) {
-      float x[4][8];
+    const T *dO = (const T *)a.dout + bh * a.N * d + c * 8;
+    // NF rows in flight per lane (raw, converted when added); each lane
+    // still adds its tokens in increasing order
+    constexpr int NF = sizeof(T) == 2 ? 16 : 8;
+    for (int64_t t = t0 + u; t < t1; t += NF * TL) {
+      Raw8<T> x[NF];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (t + k * TL < t1) load8(dO + (t + k * TL) * d + c * 8, x[k]);
+      for (int k = 0; k < NF; ++k)
+        if (t + k * TL < t1) x[k].load(dO + (t + k * TL) * d);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (t + k * TL < t1) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] += x[k][i];
-        }
+      for (int k = 0; k < NF; ++k)
+        if (t + k * TL < t1) x[k].add_to(acc);
     }
 #pragma unroll
     for (int off = CPR; off < 64; off <<= 1)
@@ -336,12 +370,15 @@ lh_status launch_dos_prep(const Geo &g, const float *dos, const float *os, bf16_
 
 // ---------------------------------------------------------------- unpool
 // dx[t] = sum_l dxs[row_of(l, t / p^l)] / p^l over the selected ancestors of
-// t.  One workgroup covers `spw` whole strata of one (b, h) and one tensor:
-// the strata's row_of entries (their subtrees) are staged in LDS, so lookups
-// are LDS reads.  A thread walks level-1 entries (CPR lanes per row): the
-// levels L-1..1 part, shared by the entry's p tokens, is summed once
-// (coarsest first), then each token adds its own level-0 row when selected.
-// The summation order is fixed, so results are reproducible.
+// t.  One workgroup covers `spw` whole strata of one (b, h) and one tensor.
+// Their row_of entries are staged in LDS level by level (level l of strata
+// m0 .. m0+spw-1 is one contiguous run of row_of), so the level-l ancestor of
+// workgroup-local token u sits at lb[l] + u / p^l.  A thread owns a
+// contiguous run of level-1 entries (CPR lanes per row).  Levels L-1 .. 2 are
+// summed once per level-2 cell (coarsest first) and kept; each entry adds its
+// level-1 row, converts that sum once, and every token without a level-0 row
+// of its own stores it unchanged; the others add their row.  The summation
+// order is fixed, so results are reproducible.
 constexpr int kUnpoolThreads = 256;
 constexpr int kUnpoolLdsEntries = 8192;   // row_of entries staged per workgroup
 
@@ -351,78 +388,122 @@ struct UnpoolArgs {
   const int32_t *row_of;
   int64_t N, E, S, Bc;
   int32_t d, L, p, spw, lgp;    // lgp = log2(p) when p is a power of two, else -1
-  int32_t T;                 // subtree entries per stratum
-  int64_t loff[kMaxLevels], pw[kMaxLevels];
-  int32_t cstart[kMaxLevels];   // first entry of level l inside a stratum's subtree
+  int64_t loff[kMaxLevels];
+  int32_t per[kMaxLevels];      // entries of level l per stratum (Bc / p^l)
+  int32_t pw[kMaxLevels];       // p^l
+  int32_t lb[kMaxLevels];       // first LDS slot of level l (spw * entries below it)
   float inv[kMaxLevels];
+};
+
+// 8 output values in the output dtype, as stored by one 16- or 32-byte write
+template <typename TO> struct Pack8;
+template <> struct Pack8<bf16_t> {
+  uint4 w;
+  __device__ void set(const float *x) {
+    w = make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]), pack2_bf16(x[4], x[5]),
+                   pack2_bf16(x[6], x[7]));
+  }
+  __device__ void put(bf16_t *p) const { *reinterpret_cast<uint4 *>(p) = w; }
+};
+template <> struct Pack8<float> {
+  float4 a, b;
+  __device__ void set(const float *x) {
+    a = make_float4(x[0], x[1], x[2], x[3]);
+    b = make_float4(x[4], x[5], x[6], x[7]);
+  }
+  __device__ void put(float *p) const {
+    *reinterpret_cast<float4 *>(p) = a;
+    *reinterpret_cast<float4 *>(p + 4) = b;
+  }
 };
 
 template <typename TO, int CPR>
 __global__ __launch_bounds__(kUnpoolThreads) void unpool_kernel(UnpoolArgs a) {
-  __shared__ int32_t ro[kUnpoolLdsEntries];
+  extern __shared__ int32_t ro[];
   const int z = blockIdx.z;
   const int64_t bh = blockIdx.y;
   const int64_t m0 = (int64_t)blockIdx.x * a.spw;   // first stratum of the workgroup
   const int tid = threadIdx.x;
   const int32_t *rog = a.row_of + bh * a.E;
-  // stage row_of of the spw subtrees: entry (s, l, j) at s*T + cstart[l] + j
-  for (int i = tid; i < a.spw * a.T; i += kUnpoolThreads) {
-    const int sidx = i / a.T, e = i % a.T;
-    int l = 0;
-    while (l + 1 < a.L && e >= a.cstart[l + 1]) ++l;
-    const int64_t per = a.Bc / a.pw[l];
-    const int32_t r = rog[a.loff[l] + (m0 + sidx) * per + (e - a.cstart[l])];
-    ro[i] = (r >= 0 && r < a.S) ? r : -1;
+  for (int l = 0; l < a.L; ++l) {
+    const int cnt = a.spw * a.per[l];
+    const int32_t *src = rog + a.loff[l] + m0 * a.per[l];
+    for (int i = tid; i < cnt; i += kUnpoolThreads) {
+      const int32_t r = src[i];
+      ro[a.lb[l] + i] = (r >= 0 && r < a.S) ? r : -1;
+    }
   }
   __syncthreads();
   const int c = tid % CPR;
   constexpr int LANES = kUnpoolThreads / CPR;   // lanes along the tokens
   const int d = a.d;
-  const float *dxs = a.dxs[z] + bh * a.S * d;
-  TO *out = (TO *)a.dx[z] + bh * a.N * d;
-  const int64_t t0 = m0 * a.Bc;
+  const float *dxs = a.dxs[z] + bh * a.S * d + c * 8;
+  TO *out = (TO *)a.dx[z] + (bh * a.N + m0 * a.Bc) * d + c * 8;
   const int ntok = a.spw * (int)a.Bc;
-  // work unit: one level-1 entry (p tokens; a single token when L == 1),
-  // whose tokens share every ancestor above level 0
-  const int P1 = a.L >= 2 ? a.p : 1;
+  const int P1 = a.L >= 2 ? a.p : 1;    // tokens per level-1 entry
   const int nent = ntok / P1;
-  const int per = (nent + LANES - 1) / LANES;
-  const int e_begin = (tid / CPR) * per, e_end = min(nent, e_begin + per);
+  const int span = (nent + LANES - 1) / LANES;
+  const int e_begin = (tid / CPR) * span, e_end = min(nent, e_begin + span);
+  auto anc = [&](int u, int l) { return a.lgp >= 0 ? (u >> (a.lgp * l)) : u / a.pw[l]; };
+  float A2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) A2[i] = 0.f;
+  int cell = -1;
   for (int e = e_begin; e < e_end; ++e) {
     const int u0 = e * P1;
-    const int sidx = u0 / (int)a.Bc, ul = u0 - sidx * (int)a.Bc;
-    const int base = sidx * a.T;
-    // coarse part: levels L-1 .. 1, coarsest first
+    if (a.L >= 3 && anc(u0, 2) != cell) {   // levels L-1 .. 2, coarsest first
+      cell = anc(u0, 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) A2[i] = 0.f;
+      for (int l = a.L - 1; l >= 2; --l) {
+        const int32_t r = ro[a.lb[l] + anc(u0, l)];
+        if (r >= 0) {
+          float x[8];
+          load8(dxs + (int64_t)r * d, x);
+          const float w = a.inv[l];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) A2[i] += x[i] * w;
+        }
+      }
+    }
     float A[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) A[i] = 0.f;
-    for (int l = a.L - 1; l >= 1; --l) {
-      const int j = a.lgp >= 0 ? (ul >> (a.lgp * l)) : (int)(ul / a.pw[l]);
-      const int32_t r = ro[base + a.cstart[l] + j];
+    for (int i = 0; i < 8; ++i) A[i] = A2[i];
+    if (a.L >= 2) {
+      const int32_t r = ro[a.lb[1] + e];
       if (r >= 0) {
         float x[8];
-        load8(dxs + (int64_t)r * d + c * 8, x);
-        const float w = a.inv[l];
+        load8(dxs + (int64_t)r * d, x);
+        const float w = a.inv[1];
 #pragma unroll
         for (int i = 0; i < 8; ++i) A[i] += x[i] * w;
       }
     }
-    // the entry's tokens: A plus their own level-0 row when selected
+    Pack8<TO> shared_row;
+    shared_row.set(A);
+    TO *orow = out + (int64_t)u0 * d;
     for (int k0 = 0; k0 < P1; k0 += 4) {
       float x[4][8];
       int32_t r[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        r[k] = k0 + k < P1 ? ro[base + ul + k0 + k] : -1;   // level 0 starts at entry 0
-        if (r[k] >= 0) load8(dxs + (int64_t)r[k] * d + c * 8, x[k]);
+        r[k] = k0 + k < P1 ? ro[u0 + k0 + k] : -1;   // level 0 starts at slot 0
+        if (r[k] >= 0) load8(dxs + (int64_t)r[k] * d, x[k]);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         if (k0 + k >= P1) break;
-        float o[8];
+        TO *dst = orow + (k0 + k) * d;
+        if (r[k] >= 0) {
+          float o[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = r[k] >= 0 ? A[i] + x[k][i] : A[i];
-        store8(out + (t0 + u0 + k0 + k) * d + c * 8, o);
+          for (int i = 0; i < 8; ++i) o[i] = A[i] + x[k][i];
+          Pack8<TO> v;
+          v.set(o);
+          v.put(dst);
+        } else {
+          shared_row.put(dst);
+        }
       }
     }
   }
@@ -441,26 +522,28 @@ lh_status launch_unpool(const Geo &g, const float *const dxs[3], const int32_t *
   UnpoolArgs a;
   for (int i = 0; i < 3; ++i) { a.dxs[i] = dxs[i]; a.dx[i] = dx[i]; }
   a.row_of = row_of; a.N = g.N; a.E = g.E; a.S = g.S; a.Bc = g.Bc; a.d = g.d; a.L = g.L;
-  a.p = g.p; a.T = (int32_t)g.T;
+  a.p = g.p;
   a.spw = unpool_spw(g);
   a.lgp = -1;
   for (int k = 0; k < 31; ++k)
     if ((1 << k) == g.p) a.lgp = k;
-  int cs = 0;
+  int lb = 0;
   for (int l = 0; l < kMaxLevels; ++l) {
     a.loff[l] = g.loff[l];
-    a.pw[l] = g.pw[l];
-    a.inv[l] = (float)(1.0 / (double)g.pw[l]);
-    a.cstart[l] = cs;
-    if (l < g.L) cs += (int)(g.Bc / g.pw[l]);
+    a.pw[l] = l < g.L ? (int32_t)g.pw[l] : 0;
+    a.per[l] = l < g.L ? (int32_t)(g.Bc / g.pw[l]) : 0;
+    a.inv[l] = l < g.L ? (float)(1.0 / (double)g.pw[l]) : 0.f;
+    a.lb[l] = lb;
+    lb += a.spw * a.per[l];
   }
+  const size_t smem = (size_t)a.spw * g.T * sizeof(int32_t);
   dim3 grid((unsigned)(g.n_c / a.spw), (unsigned)g.BH(), 3);
   if (g.out == LH_BF16) {
-    if (g.d == 128) hipLaunchKernelGGL((unpool_kernel<bf16_t, 16>), grid, dim3(kUnpoolThreads), 0, st, a);
-    else hipLaunchKernelGGL((unpool_kernel<bf16_t, 8>), grid, dim3(kUnpoolThreads), 0, st, a);
+    if (g.d == 128) hipLaunchKernelGGL((unpool_kernel<bf16_t, 16>), grid, dim3(kUnpoolThreads), smem, st, a);
+    else hipLaunchKernelGGL((unpool_kernel<bf16_t, 8>), grid, dim3(kUnpoolThreads), smem, st, a);
   } else {
-    if (g.d == 128) hipLaunchKernelGGL((unpool_kernel<float, 16>), grid, dim3(kUnpoolThreads), 0, st, a);
-    else hipLaunchKernelGGL((unpool_kernel<float, 8>), grid, dim3(kUnpoolThreads), 0, st, a);
+    if (g.d == 128) hipLaunchKernelGGL((unpool_kernel<float, 16>), grid, dim3(kUnpoolThreads), smem, st, a);
+    else hipLaunchKernelGGL((unpool_kernel<float, 8>), grid, dim3(kUnpoolThreads), smem, st, a);
   }
   return hip_status();
 }

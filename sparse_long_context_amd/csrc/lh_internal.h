@@ -37,12 +37,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// float32 -> bfloat16 with round-to-nearest-even (NaN kept quiet)
+// float32 -> bfloat16, round-to-nearest-even, with the hardware packed
+// convert (v_cvt_pk_bf16_f32); it matches a software RNE on every non-NaN
+// input and maps NaN to a quiet NaN
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const f32x2_hw v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
+}
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
 template <typename T> struct Elem;
@@ -77,11 +82,8 @@ __device__ __forceinline__ void store8(float *p, const float *x) {
   *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
 __device__ __forceinline__ void store8(bf16_t *p, const float *x) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
-  *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4 *>(p) = make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]),
+                                             pack2_bf16(x[4], x[5]), pack2_bf16(x[6], x[7]));
 }
 
 // two-term bf16 split of 8 floats: hi = bf16(x), lo = bf16(x - hi), so that
