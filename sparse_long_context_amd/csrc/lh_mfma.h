@@ -52,11 +52,19 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const f32x16 &acc, int o) {
 // pair carries about 16 significant bits, so a product taken as
 // hi*B + lo*B loses far less than one rounding of x to bf16
 __device__ __forceinline__ void pack_split(const f32x16 &acc, int o, bf16x8 &hi, bf16x8 &lo) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 h = (__bf16)acc[o + e];
-    hi[e] = h;
-    lo[e] = (__bf16)(acc[o + e] - (float)h);
+  for (int e = 0; e < 8; e += 2) {
+    const f2 x = {acc[o + e], acc[o + e + 1]};
+    const b2 h = __builtin_convertvector(x, b2);   // one packed convert per pair
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    const f2 hf = {__uint_as_float(hb << 16), __uint_as_float(hb & 0xffff0000u)};
+    const b2 l = __builtin_convertvector(x - hf, b2);
+    hi[e] = h[0];
+    hi[e + 1] = h[1];
+    lo[e] = l[0];
+    lo[e + 1] = l[1];
   }
 }
 
@@ -104,15 +112,20 @@ __device__ __forceinline__ bf16x8 ld_colop(const bf16_t *X, int s, int nb, int l
   const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, ab);
 }
-// async global -> LDS copy of `rows` rows of a [*, D] bf16 matrix (row stride
-// D) into a swizzled row tile, by the `nthr` threads t = 0..nthr-1 (whole
-// wavefronts); rows past `rmax` repeat row rmax
-template <int D>
+// async global -> LDS copy of ROWS rows of a [*, D] bf16 matrix (row stride
+// D) into a swizzled row tile, by the NTHR threads t = 0..NTHR-1 (whole
+// wavefronts, each issuing the same number of 1 KB pieces); rows past `rmax`
+// repeat row rmax
+template <int D, int ROWS, int NTHR>
 __device__ __forceinline__ void tile_load(bf16_t *dst, const bf16_t *src, int64_t row0,
-                                          int64_t rmax, int rows, int t, int nthr) {
+                                          int64_t rmax, int t) {
+  constexpr int PIECES = ROWS * D / 8 / 64;
+  constexpr int WAVES = NTHR / 64;
+  static_assert(PIECES % WAVES == 0, "pieces split evenly over the wavefronts");
   const int lane = t & 63, w = t >> 6;
-  const int pieces = rows * D / 8 / 64;   // 1 KB pieces
-  for (int j = w; j < pieces; j += nthr / 64) {
+#pragma unroll
+  for (int i = 0; i < PIECES / WAVES; ++i) {
+    const int j = w + i * WAVES;
     const int chunk = j * 64 + lane;
     const int r = chunk / (D / 8), p = chunk % (D / 8);
     const int c = p ^ swz_r<D>(r);
