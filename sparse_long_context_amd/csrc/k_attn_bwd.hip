@@ -137,41 +137,40 @@ void attn_bwd_dkv_kernel(
   // after the barrier).  A wavefront computes S and dP of block qb + 1 while
   // it turns block qb's S and dP into P and dS and adds block qb's dV and dK:
   // the two halves are independent, so MFMAs overlap the exponentials.
-  auto step = [&](int qb) {
+  auto sync = [&](int qb) {
     kv_wait<D>(qb + 2 < nqb, w == 0);
-    __syncthreads();
-    if (qb + 3 < nqb)
-      kv_issue<D>(stg[(qb + 3) % kKvStages], Q, DH, DL, LSE, DR, (int64_t)(qb + 3) * kKvBQ, S,
-                  tid);
+    lds_barrier();
   };
-  // S = Q K^T and dP = dO V^T of block qb (lane: key column; rows: queries 8I + 4h + J)
-  auto sdp = [&](int qb, f32x16 &sa, f32x16 &dp) {
-    const KvStage<D> &sb = stg[qb % kKvStages];
+  auto issue = [&](KvStage<D> *st, int qb) {
+    if (qb + 3 < nqb)
+      kv_issue<D>(*st, Q, DH, DL, LSE, DR, (int64_t)(qb + 3) * kKvBQ, S, tid);
+  };
+  auto slot = [&](int qb) { return &stg[(qb + kKvStages) % kKvStages]; };
+  // S = Q K^T and dP = dO V^T of a block (lane: key column; rows: queries 8I + 4h + J)
+  auto sdp = [&](const KvStage<D> *sb, f32x16 &sa, f32x16 &dp) {
     sa = zero16();
     dp = zero16();
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      sa = mfma32(ld_rowop<D>(sb.q, col, s, h), kreg[s], sa);
-      dp = mfma32(ld_rowop<D>(sb.dh, col, s, h), vreg[s], dp);
-      dp = mfma32(ld_rowop<D>(sb.dl, col, s, h), vreg[s], dp);
+      sa = mfma32(ld_rowop<D>(sb->q, col, s, h), kreg[s], sa);
+      dp = mfma32(ld_rowop<D>(sb->dh, col, s, h), vreg[s], dp);
+      dp = mfma32(ld_rowop<D>(sb->dl, col, s, h), vreg[s], dp);
     }
   };
   // P, dS of block qb from its S, dP (in place).  EDGE blocks (the one on
   // the wavefront's diagonal, the one crossing S) mask by index; inside the
   // range only dead keys are masked, through an infinite lse.
   const float dead_lse = dead ? INFINITY : 0.f;
-  auto softmax = [&](auto edge_tag, int qb, f32x16 &sa, f32x16 &dp) {
+  auto softmax = [&](auto edge_tag, const KvStage<D> *sb, int qb, f32x16 &sa, f32x16 &dp) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const KvStage<D> &sb = stg[qb % kKvStages];
     const int64_t q0 = (int64_t)qb * kKvBQ;
     const int kr = (int)(key - q0);                       // causal: query index >= kr
     const int qn = (int)min((int64_t)kKvBQ, S - q0);      // queries of the block inside S
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       const int ql = 8 * I + 4 * h;
-      const float4 lv = *reinterpret_cast<const float4 *>(sb.lse + ql);
-      const float4 dv = *reinterpret_cast<const float4 *>(sb.drow + ql);
-      const float lj[4] = {lv.x, lv.y, lv.z, lv.w}, dj[4] = {dv.x, dv.y, dv.z, dv.w};
+      const f32x4 lj = *reinterpret_cast<const f32x4 *>(sb->lse + ql);
+      const f32x4 dj = *reinterpret_cast<const f32x4 *>(sb->drow + ql);
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         const int v = 4 * I + J;
@@ -185,16 +184,15 @@ void attn_bwd_dkv_kernel(
       }
     }
   };
-  // the B operands of one 16-query step of block qb: dO hi, dO lo, Q
+  // the B operands of one 16-query step of a block: dO hi, dO lo, Q
   // columns for every 32-column block of the head dimension
   struct ColOps { bf16x8 dh[DB], dl[DB], q[DB]; };
-  auto colops = [&](int qb, int s2, ColOps &c) {
-    const KvStage<D> &sb = stg[qb % kKvStages];
+  auto colops = [&](const KvStage<D> *sb, int s2, ColOps &c) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      c.dh[b] = ld_colop<D>(sb.dh, s2, 32 * b, lane);
-      c.dl[b] = ld_colop<D>(sb.dl, s2, 32 * b, lane);
-      c.q[b] = ld_colop<D>(sb.q, s2, 32 * b, lane);
+      c.dh[b] = ld_colop<D>(sb->dh, s2, 32 * b, lane);
+      c.dl[b] = ld_colop<D>(sb->dl, s2, 32 * b, lane);
+      c.q[b] = ld_colop<D>(sb->q, s2, 32 * b, lane);
     }
   };
   // dV += P^T dO and dK += dS^T Q over one 16-query step
@@ -211,44 +209,44 @@ void attn_bwd_dkv_kernel(
       acc_dk[b] = mfma32(asl, c.q[b], acc_dk[b]);
     }
   };
-  auto grad = [&](int qb, f32x16 sa, f32x16 dp) {   // edge blocks only
-    softmax(std::true_type(), qb, sa, dp);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      ColOps c;
-      colops(qb, s2, c);
-      accum(sa, dp, s2, c);
-    }
-  };
 
   // first block with queries at or past this wavefront's keys
   const int f = all_dead ? nqb : (int)(kw0 / kKvBQ);
   int qb = qb0 - 1;
   if (f >= nqb) {
-    for (; qb < nqb; ++qb) step(qb);
+    for (; qb < nqb; ++qb) {
+      sync(qb);
+      issue(slot(qb + 3), qb);
+    }
   } else {
-    for (; qb < f - 1; ++qb) step(qb);
+    for (; qb < f - 1; ++qb) {
+      sync(qb);
+      issue(slot(qb + 3), qb);
+    }
     f32x16 sa, dp;
-    step(qb);
-    sdp(f, sa, dp);
-    // block f (the diagonal) has the index mask; later blocks up to nqb - 2
-    // lie inside the range; block nqb - 1 goes through grad below
-    auto iter = [&](auto edge_tag) {
-      constexpr bool EDGE = decltype(edge_tag)::value;
-      step(qb);
-      // One wavefront per SIMD: no other wavefront hides LDS latency or the
-      // exponentials, so the iteration is laid out by hand in fenced regions:
-      // (1) all row-operand reads of block qb + 1; (2) its S and dP MFMAs
-      // with block qb's exponentials between them, and the column operands
-      // of block qb's first query step; (3) that step's MFMAs with the second
-      // step's reads; (4) the second step's MFMAs.
-      const KvStage<D> &sn_ = stg[(qb + 1) % kKvStages];
+    sync(qb);
+    issue(slot(qb + 3), qb);
+    sdp(slot(f), sa, dp);
+    // One steady iteration (block qb; the slots are distinct, which the
+    // restrict qualifiers state, so the compiler does not make LDS reads
+    // wait for the global->LDS loads into `fill`; the explicit vmcnt before
+    // each barrier is what orders them).  One wavefront per SIMD: no other
+    // wavefront hides LDS latency or the exponentials, so the iteration is
+    // laid out by hand in fenced regions: (1) all row-operand reads of block
+    // qb + 1; (2) its S and dP MFMAs with block qb's exponentials between
+    // them, and the column operands of block qb's first query step; (3) that
+    // step's MFMAs with the second step's reads; (4) the second step's MFMAs.
+    // Block f (the diagonal) has the index mask; later blocks up to nqb - 2
+    // lie inside the range; block nqb - 1 goes through the tail below.
+    auto iter = [&](auto edge_tag, KvStage<D> *__restrict__ fill,
+                    const KvStage<D> *__restrict__ cur, const KvStage<D> *__restrict__ nxt) {
+      issue(fill, qb);
       bf16x8 ra[KSTEPS], rh[KSTEPS], rl[KSTEPS];
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        ra[s] = ld_rowop<D>(sn_.q, col, s, h);
-        rh[s] = ld_rowop<D>(sn_.dh, col, s, h);
-        rl[s] = ld_rowop<D>(sn_.dl, col, s, h);
+        ra[s] = ld_rowop<D>(nxt->q, col, s, h);
+        rh[s] = ld_rowop<D>(nxt->dh, col, s, h);
+        rl[s] = ld_rowop<D>(nxt->dl, col, s, h);
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x16 sn = zero16(), dn = zero16();
@@ -258,12 +256,12 @@ void attn_bwd_dkv_kernel(
         dn = mfma32(rh[s], vreg[s], dn);
         dn = mfma32(rl[s], vreg[s], dn);
       }
-      softmax(edge_tag, qb, sa, dp);
+      softmax(edge_tag, cur, qb, sa, dp);
       ColOps c0;
-      colops(qb, 0, c0);
+      colops(cur, 0, c0);
       __builtin_amdgcn_sched_barrier(0);
       ColOps c1;
-      colops(qb, 1, c1);
+      colops(cur, 1, c1);
       accum(sa, dp, 0, c0);
       __builtin_amdgcn_sched_barrier(0);
       accum(sa, dp, 1, c1);
@@ -272,11 +270,21 @@ void attn_bwd_dkv_kernel(
     };
     qb = f;
     if (qb < nqb - 1) {
-      iter(std::true_type());
-      for (++qb; qb < nqb - 1; ++qb) iter(std::false_type());
+      sync(qb);
+      iter(std::true_type(), slot(qb + 3), slot(qb), slot(qb + 1));
+      for (++qb; qb < nqb - 1; ++qb) {
+        sync(qb);
+        iter(std::false_type(), slot(qb + 3), slot(qb), slot(qb + 1));
+      }
     }
-    step(qb);
-    grad(qb, sa, dp);
+    sync(qb);   // qb == nqb - 1: nothing left to issue
+    softmax(std::true_type(), slot(qb), qb, sa, dp);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      ColOps c;
+      colops(slot(qb), s2, c);
+      accum(sa, dp, s2, c);
+    }
   }
 
   // lane: head-dim column b*32 + col; rows are keys kw0 + 8I + 4h + J
@@ -293,147 +301,221 @@ void attn_bwd_dkv_kernel(
 }
 
 // ---------------------------------------------------------------- dQ
-constexpr int kQBQ = 128;   // queries per workgroup
-constexpr int kQBK = 32;    // keys per block
+constexpr int kQBQ = 128;      // queries per workgroup (32 per wavefront)
+constexpr int kQBK = 32;       // keys per block
+constexpr int kQThreads = 256;
+constexpr int kQStages = 4;    // LDS ring: two blocks in use, two loading
 
 template <int D>
-struct QSmem {
-  bf16_t k[2][2][kQBK * D];   // [group][buffer] K rows
-  bf16_t v[2][2][kQBK * D];   // V rows
-  float bias[2][2][kQBK];
+struct QStage {
+  bf16_t k[kQBK * D];   // K rows of the block
+  bf16_t v[kQBK * D];   // V rows
+  float bias[kQBK];     // 0, or -inf for a redundant key or one past S
 };
 
 template <int D>
-__global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dq_kernel(
     const bf16_t *__restrict__ qs, const bf16_t *__restrict__ ks, const bf16_t *__restrict__ vs,
     const bf16_t *__restrict__ doh, const bf16_t *__restrict__ dol,
     const float *__restrict__ lse, const float *__restrict__ drow,
     const uint8_t *__restrict__ flags, float *__restrict__ dqs, int64_t S, int32_t BH,
     float scale) {
+  static_assert(kQStages == 4, "block kb + 3 is issued into the slot of block kb - 1");
   extern __shared__ __align__(16) unsigned char smraw[];
-  QSmem<D> &sm = *reinterpret_cast<QSmem<D> *>(smraw);
+  QStage<D> *stg = reinterpret_cast<QStage<D> *>(smraw);
+  uint8_t *fl_lds = smraw + sizeof(QStage<D>) * kQStages;   // flags of keys 0 .. kend-1
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int L = 2 * (kQBK * D / 8 / 64) / 4;   // tile loads per wavefront per block
 
   const int nqb = (int)((S + kQBQ - 1) / kQBQ);
   const int item = (int)blockIdx.x;
   const int qb = nqb - 1 - item / BH;             // heaviest first
   const int64_t bh = item % BH;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int grp = wave >> 2, w = wave & 3, gtid = tid & 255;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 31, h = lane >> 5;
   const int64_t q0w = (int64_t)qb * kQBQ + w * 32;
   const int64_t q = q0w + col;
   const float sl2 = scale * kLog2e;
-
   const bf16_t *Kg = ks + bh * S * D, *Vg = vs + bh * S * D;
-  const uint8_t *fl = flags + bh * S;
 
-  bf16x8 qreg[KSTEPS], dregh[KSTEPS], dregl[KSTEPS];
+  const int64_t kend = min(S, (int64_t)(qb + 1) * kQBQ);
+  const int nkb = (int)((kend + kQBK - 1) / kQBK);
   {
-    const int64_t qc = min(q, S - 1);   // rows past S are never stored
+    // flags of the workgroup's key range, 16 loads in flight per thread
+    constexpr int FPT = 16;
+    for (int64_t i0 = 0; i0 < kend; i0 += (int64_t)FPT * kQThreads) {
+      uint8_t v[FPT];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      qreg[s] = ld_bf16x8(qs + (bh * S + qc) * D + s * 16 + 8 * h);
-      dregh[s] = ld_bf16x8(doh + (bh * S + qc) * D + s * 16 + 8 * h);
-      dregl[s] = ld_bf16x8(dol + (bh * S + qc) * D + s * 16 + 8 * h);
+      for (int j = 0; j < FPT; ++j) {
+        const int64_t i = i0 + (int64_t)j * kQThreads + tid;
+        v[j] = i < kend ? flags[bh * S + i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < FPT; ++j) {
+        const int64_t i = i0 + (int64_t)j * kQThreads + tid;
+        if (i < kend) fl_lds[i] = v[j];
+      }
     }
   }
-  const float lse2 = q < S ? lse[bh * S + q] * kLog2e : INFINITY;
-  const float dr = q < S ? drow[bh * S + q] : 0.f;
 
+  // this lane's query: Q and dO (hi, lo) are the B operands of S^T = K Q^T
+  // and dP^T = V dO^T
+  bf16x8 qreg[KSTEPS], dregh[KSTEPS], dregl[KSTEPS];
+  {
+    const int64_t qc = (bh * S + min(q, S - 1)) * D + 8 * h;   // rows past S are never stored
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      qreg[s] = ld_bf16x8(qs + qc + s * 16);
+      dregh[s] = ld_bf16x8(doh + qc + s * 16);
+      dregl[s] = ld_bf16x8(dol + qc + s * 16);
+    }
+  }
+  const float lse2 = q < S ? lse[bh * S + q] * kLog2e : 0.f;
+  const float dr = q < S ? drow[bh * S + q] : 0.f;
+  // a wait the compiler sees: the register loads above are complete before
+  // the loop (otherwise it re-waits for them inside every iteration)
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+  auto issue = [&](QStage<D> *st, int kb) {   // block kb + 3 into st
+    if (kb + 3 < nkb) {
+      tile_load<D, kQBK, kQThreads>(st->k, Kg, (int64_t)(kb + 3) * kQBK, S - 1, tid);
+      tile_load<D, kQBK, kQThreads>(st->v, Vg, (int64_t)(kb + 3) * kQBK, S - 1, tid);
+    }
+  };
+  auto slot = [&](int kb) { return &stg[(kb + kQStages) % kQStages]; };
+  for (int j = 0; j < 2; ++j) issue(slot(j), j - 3);
   f32x16 acc_dq[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc_dq[b] = zero16();
 
-  const int64_t kend = min(S, (int64_t)(qb + 1) * kQBQ);
-  const int nkb = (int)((kend + kQBK - 1) / kQBK);
-  const int niter = (nkb + 1) / 2;
-
-#define LH_Q_ISSUE(kb_, buf_)                                                                 \
-  do {                                                                                        \
-    const int64_t r0 = (int64_t)(kb_) * kQBK;                                                 \
-    tile_load<D, kQBK, 256>(sm.k[grp][buf_], Kg, r0, S - 1, gtid);                             \
-    tile_load<D, kQBK, 256>(sm.v[grp][buf_], Vg, r0, S - 1, gtid);                             \
-  } while (0)
-#define LH_Q_BIAS(kb_)                                                                        \
-  ([&]() -> float {                                                                           \
-    const int64_t kk_ = (int64_t)(kb_) * kQBK + (gtid & 31);                                  \
-    return (kk_ < S && !(fl[kk_] & LH_ROW_REDUNDANT)) ? 0.f : -INFINITY;                      \
-  }())
-
-  if (grp < nkb) {
-    LH_Q_ISSUE(grp, 0);
-    const float bv = LH_Q_BIAS(grp);
-    if (gtid < kQBK) sm.bias[grp][0][gtid] = bv;
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int it = 0; it < niter; ++it) {
-    const int kb = 2 * it + grp, kbn = kb + 2, buf = it & 1;
-    float bnext = 0.f;
-    if (kbn < nkb) {
-      LH_Q_ISSUE(kbn, buf ^ 1);
-      bnext = LH_Q_BIAS(kbn);
+  // Iteration kb (-1 .. nkb - 1) waits for block kb + 1, has wavefront 0
+  // turn that block's flags into its bias slot, and issues block kb + 3 into
+  // the slot of block kb - 1.
+  auto sync = [&](int kb) {
+    if (kb + 2 >= nkb) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
+    lds_barrier();
+    if (w == 0 && lane < kQBK && kb + 1 < nkb) {
+      const int64_t kk = (int64_t)(kb + 1) * kQBK + lane;
+      slot(kb + 1)->bias[lane] = (kk < kend && !(fl_lds[kk] & LH_ROW_REDUNDANT)) ? 0.f : -INFINITY;
     }
-    const int64_t k0 = (int64_t)kb * kQBK;
-    if (kb < nkb && k0 <= q0w + 31) {   // wavefront-uniform
-      const bf16_t *tk = sm.k[grp][buf], *tv = sm.v[grp][buf];
-      const float *bias = sm.bias[grp][buf];
-      // S^T = K Q^T, dP^T = V dO^T (lane: query column; rows: keys 8I + 4h + J)
-      f32x16 sacc = zero16(), dpacc = zero16();
+  };
+  // S^T = K Q^T and dP^T = V dO^T of a block (lane: query column; rows:
+  // keys 8I + 4h + J)
+  auto sdp = [&](const QStage<D> *sb, f32x16 &sa, f32x16 &dp) {
+    sa = zero16();
+    dp = zero16();
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      sa = mfma32(ld_rowop<D>(sb->k, col, s, h), qreg[s], sa);
+      const bf16x8 av = ld_rowop<D>(sb->v, col, s, h);
+      dp = mfma32(av, dregh[s], dp);
+      dp = mfma32(av, dregl[s], dp);
+    }
+  };
+  // dS^T of block kb from its S^T, dP^T (in place); EDGE: the block on the
+  // wavefront's diagonal (keys past the query masked)
+  auto softmax = [&](auto edge_tag, const QStage<D> *sb, int kb, f32x16 &sa, f32x16 &dp) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int qr = (int)(q - (int64_t)kb * kQBK);   // causal: key index <= qr
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const int kl = 8 * I + 4 * h;
+      const f32x4 bj = *reinterpret_cast<const f32x4 *>(sb->bias + kl);
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const int v = 4 * I + J;
+        float x = sa[v] * sl2 + (bj[J] - lse2);
+        if constexpr (EDGE) x = kl + J > qr ? -INFINITY : x;
+        const float p = __builtin_amdgcn_exp2f(x);
+        dp[v] = p * (dp[v] - dr);
+      }
+    }
+  };
+  // the A operands of one 16-key step: K^T through the transposing read
+  auto colops = [&](const QStage<D> *sb, int s2, bf16x8 (&a)[DB]) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b) a[b] = ld_colop<D>(sb->k, s2, 32 * b, lane);
+  };
+  // dQ^T += K^T dS^T over one 16-key step
+  auto accum = [&](const f32x16 &ds, int s2, const bf16x8 (&a)[DB]) {
+    bf16x8 bsh, bsl;
+    pack_split(ds, 8 * s2, bsh, bsl);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      acc_dq[b] = mfma32(a[b], bsh, acc_dq[b]);
+      acc_dq[b] = mfma32(a[b], bsl, acc_dq[b]);
+    }
+  };
+
+  // last key block of this wavefront (its diagonal, or the last one of S)
+  const int lw = q0w < S ? (int)min((int64_t)nkb - 1, (q0w + 31) / kQBK) : -1;
+  int kb = -1;
+  if (lw < 0) {
+    for (; kb < nkb; ++kb) {
+      sync(kb);
+      issue(slot(kb + 3), kb);
+    }
+  } else {
+    f32x16 sa, dp;
+    sync(kb);
+    issue(slot(kb + 3), kb);
+    sdp(slot(0), sa, dp);
+    // steady iterations: S^T, dP^T of block kb + 1 in fenced regions with
+    // block kb's exponentials and dQ (one wavefront per SIMD, so the issue
+    // order is laid out by hand, as in the dK/dV kernel; the restrict
+    // qualifiers state that the slots are distinct)
+    auto iter = [&](QStage<D> *__restrict__ fill, const QStage<D> *__restrict__ cur,
+                    const QStage<D> *__restrict__ nxt) {
+      issue(fill, kb);
+      bf16x8 rk[KSTEPS], rv[KSTEPS];
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        sacc = mfma32(ld_rowop<D>(tk, col, s, h), qreg[s], sacc);
-        const bf16x8 av = ld_rowop<D>(tv, col, s, h);
-        dpacc = mfma32(av, dregh[s], dpacc);
-        dpacc = mfma32(av, dregl[s], dpacc);
+        rk[s] = ld_rowop<D>(nxt->k, col, s, h);
+        rv[s] = ld_rowop<D>(nxt->v, col, s, h);
       }
-      const bool diag = k0 + kQBK - 1 > q0w;
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 sn = zero16(), dn = zero16();
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const int kl = 8 * I + 4 * h;
-        const float4 bv = *reinterpret_cast<const float4 *>(bias + kl);
-        const float bj[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          const int v = 4 * I + J;
-          float p = __builtin_amdgcn_exp2f(sacc[v] * sl2 + bj[J] - lse2);
-          if (diag && k0 + kl + J > q) p = 0.f;
-          dpacc[v] = p * (dpacc[v] - dr);
-        }
+      for (int s = 0; s < KSTEPS; ++s) {
+        sn = mfma32(rk[s], qreg[s], sn);
+        dn = mfma32(rv[s], dregh[s], dn);
+        dn = mfma32(rv[s], dregl[s], dn);
       }
-      // dQ^T += K^T dS^T over two 16-key steps (K^T through the transposing read)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 bsh, bsl;
-        pack_split(dpacc, 8 * s2, bsh, bsl);
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const bf16x8 a = ld_colop<D>(tk, s2, 32 * b, lane);
-          acc_dq[b] = mfma32(a, bsh, acc_dq[b]);
-          acc_dq[b] = mfma32(a, bsl, acc_dq[b]);
-        }
-      }
+      softmax(std::false_type(), cur, kb, sa, dp);
+      bf16x8 a0[DB];
+      colops(cur, 0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 a1[DB];
+      colops(cur, 1, a1);
+      accum(dp, 0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      accum(dp, 1, a1);
+      sa = sn;
+      dp = dn;
+    };
+    for (kb = 0; kb < lw; ++kb) {
+      sync(kb);
+      iter(slot(kb + 3), slot(kb), slot(kb + 1));
     }
-    if (kbn < nkb && gtid < kQBK) sm.bias[grp][buf ^ 1][gtid] = bnext;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    sync(kb);   // kb == lw: the diagonal block
+    issue(slot(kb + 3), kb);
+    softmax(std::true_type(), slot(kb), kb, sa, dp);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 a[DB];
+      colops(slot(kb), s2, a);
+      accum(dp, s2, a);
+    }
+    for (++kb; kb < nkb; ++kb) {
+      sync(kb);
+      issue(slot(kb + 3), kb);
+    }
   }
-#undef LH_Q_ISSUE
-#undef LH_Q_BIAS
 
-  // group 1 adds its partial to group 0's through LDS
-  float *xo = reinterpret_cast<float *>(smraw);   // [DB*16][256]
-  if (grp == 1) {
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) xo[(b * 16 + v) * 256 + gtid] = acc_dq[b][v];
-  }
-  __syncthreads();
-  if (grp == 0 && q < S) {
+  if (q < S) {
     float *out = dqs + (bh * S + q) * D;
     // lane: query column; rows are head-dim 8I + 4h + J
 #pragma unroll
@@ -442,20 +524,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dq_kernel(
       for (int I = 0; I < 4; ++I) {
         float o4[4];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          const int v = 4 * I + J;
-          o4[J] = (acc_dq[b][v] + xo[(b * 16 + v) * 256 + gtid]) * scale;
-        }
+        for (int J = 0; J < 4; ++J) o4[J] = acc_dq[b][4 * I + J] * scale;
         *reinterpret_cast<float4 *>(out + b * 32 + 8 * I + 4 * h) =
             make_float4(o4[0], o4[1], o4[2], o4[3]);
       }
   }
 }
 
-template <typename Smem>
-static size_t smem_bytes(size_t merge) {
-  return sizeof(Smem) > merge ? sizeof(Smem) : merge;
-}
+constexpr size_t kMaxLds = 160 * 1024;   // LDS of one CU
 
 lh_status launch_attn_bwd_dkv_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                    const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
@@ -481,13 +557,16 @@ lh_status launch_attn_bwd_dq_bf16(const Geo &g, const bf16_t *qs, const bf16_t *
                                   const float *lse, const float *drow, const uint8_t *flags,
                                   float *dqs, hipStream_t st) {
   const unsigned items = cdiv(g.S, kQBQ) * (unsigned)g.BH();
+  // LDS: the ring, then one flag byte per key of the widest key range
+  const size_t flb = (size_t)((g.S + 15) / 16 * 16);
 #define LH_DQ(D)                                                                              \
   do {                                                                                        \
-    const size_t shm = smem_bytes<QSmem<D>>((size_t)(D / 32) * 16 * 256 * 4);               \
+    const size_t shm = sizeof(QStage<D>) * kQStages + flb;                                    \
+    if (shm > kMaxLds) return LH_ERR_UNSUPPORTED;                                             \
     (void)hipFuncSetAttribute((const void *)attn_bwd_dq_kernel<D>,                            \
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);          \
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(items), dim3(kBwdThreads), shm, st, qs,    \
-                       ks, vs, dos_hi, dos_lo, lse, drow, flags, dqs, g.S, (int32_t)g.BH(),   \
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(items), dim3(kQThreads), shm, st, qs, ks,  \
+                       vs, dos_hi, dos_lo, lse, drow, flags, dqs, g.S, (int32_t)g.BH(),       \
                        g.scale);                                                              \
   } while (0)
   if (g.d == 128) LH_DQ(128); else LH_DQ(64);

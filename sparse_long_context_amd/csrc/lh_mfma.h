@@ -112,6 +112,22 @@ __device__ __forceinline__ bf16x8 ld_colop(const bf16_t *X, int s, int nb, int l
   const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, ab);
 }
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier for LDS traffic: waits for this wavefront's LDS
+// operations only.  Outstanding global->LDS loads are not waited for here
+// (a full __syncthreads fence would drain them all); callers wait for the
+// loads they need with an explicit vmcnt first.  LDS data read after the
+// barrier should be read through native vector types (f32x4, bf16x8): a
+// read the backend splits and re-merges loses the memory information that
+// tells it the read cannot overlap a pending global->LDS load, and it then
+// waits for every such load.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // async global -> LDS copy of ROWS rows of a [*, D] bf16 matrix (row stride
 // D) into a swizzled row tile, by the NTHR threads t = 0..NTHR-1 (whole
 // wavefronts, each issuing the same number of 1 KB pieces); rows past `rmax`
