@@ -42,7 +42,7 @@ constexpr int kBwdThreads = 512;
 constexpr int kKvBK = 128;    // keys per workgroup (32 per wavefront)
 constexpr int kKvBQ = 32;     // queries per block
 constexpr int kKvThreads = 256;
-constexpr int kKvStages = 4;  // LDS ring: two blocks in use, two loading
+constexpr int kKvStages = 5;  // LDS ring: three blocks resident, two loading
 
 template <int D>
 struct KvStage {
@@ -92,7 +92,7 @@ void attn_bwd_dkv_kernel(
     const float *__restrict__ lse, const float *__restrict__ drow,
     const uint8_t *__restrict__ flags, float *__restrict__ dks, float *__restrict__ dvs,
     int64_t S, int32_t BH, float scale) {
-  static_assert(kKvStages == 4, "block qb + 3 is issued into the slot of block qb - 1");
+  static_assert(kKvStages == 5, "block qb + 4 is issued into the slot of block qb - 1");
   extern __shared__ __align__(16) unsigned char smraw[];
   KvStage<D> *stg = reinterpret_cast<KvStage<D> *>(smraw);
   constexpr int KSTEPS = D / 16;
@@ -101,7 +101,8 @@ void attn_bwd_dkv_kernel(
   const int item = (int)blockIdx.x;
   const int kb = item / BH;                      // small kb: longest query range
   const int64_t bh = item % BH;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront index, scalar
   const int col = lane & 31, h = lane >> 5;
   const int64_t kw0 = (int64_t)kb * kKvBK + w * 32;
   const int64_t key = kw0 + col;
@@ -114,7 +115,7 @@ void attn_bwd_dkv_kernel(
 
   const int qb0 = (int)((int64_t)kb * kKvBK / kKvBQ);
   const int nqb = (int)((S + kKvBQ - 1) / kKvBQ);
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 3; ++j)
     if (qb0 + j < nqb)
       kv_issue<D>(stg[(qb0 + j) % kKvStages], Q, DH, DL, LSE, DR, (int64_t)(qb0 + j) * kKvBQ, S, tid);
 
@@ -132,31 +133,21 @@ void attn_bwd_dkv_kernel(
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc_dk[b] = acc_dv[b] = zero16();
 
-  // Iteration qb (qb0 - 1 .. nqb - 1) waits for block qb + 1, then issues
-  // block qb + 3 into the slot of block qb - 1 (every wavefront is past it
+  // Iteration qb (qb0 - 1 .. nqb - 1) waits for block qb + 2, then issues
+  // block qb + 4 into the slot of block qb - 1 (every wavefront is past it
   // after the barrier).  A wavefront computes S and dP of block qb + 1 while
-  // it turns block qb's S and dP into P and dS and adds block qb's dV and dK:
-  // the two halves are independent, so MFMAs overlap the exponentials.
+  // it turns block qb's S and dP into P and dS and adds block qb's dV and dK,
+  // and it reads block qb + 2's row operands for the next iteration: the
+  // parts are independent, so MFMAs overlap the exponentials and the reads.
   auto sync = [&](int qb) {
-    kv_wait<D>(qb + 2 < nqb, w == 0);
+    kv_wait<D>(qb + 3 < nqb, w == 0);
     lds_barrier();
   };
   auto issue = [&](KvStage<D> *st, int qb) {
-    if (qb + 3 < nqb)
-      kv_issue<D>(*st, Q, DH, DL, LSE, DR, (int64_t)(qb + 3) * kKvBQ, S, tid);
+    if (qb + 4 < nqb)
+      kv_issue<D>(*st, Q, DH, DL, LSE, DR, (int64_t)(qb + 4) * kKvBQ, S, tid);
   };
   auto slot = [&](int qb) { return &stg[(qb + kKvStages) % kKvStages]; };
-  // S = Q K^T and dP = dO V^T of a block (lane: key column; rows: queries 8I + 4h + J)
-  auto sdp = [&](const KvStage<D> *sb, f32x16 &sa, f32x16 &dp) {
-    sa = zero16();
-    dp = zero16();
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      sa = mfma32(ld_rowop<D>(sb->q, col, s, h), kreg[s], sa);
-      dp = mfma32(ld_rowop<D>(sb->dh, col, s, h), vreg[s], dp);
-      dp = mfma32(ld_rowop<D>(sb->dl, col, s, h), vreg[s], dp);
-    }
-  };
   // P, dS of block qb from its S, dP (in place).  EDGE blocks (the one on
   // the wavefront's diagonal, the one crossing S) mask by index; inside the
   // range only dead keys are masked, through an infinite lse.
@@ -184,6 +175,16 @@ void attn_bwd_dkv_kernel(
       }
     }
   };
+  // the A operands of S and dP of a block: Q, dO hi, dO lo rows
+  struct RowOps { bf16x8 q[KSTEPS], dh[KSTEPS], dl[KSTEPS]; };
+  auto rowops = [&](const KvStage<D> *sb, RowOps &r) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      r.q[s] = ld_rowop<D>(sb->q, col, s, h);
+      r.dh[s] = ld_rowop<D>(sb->dh, col, s, h);
+      r.dl[s] = ld_rowop<D>(sb->dl, col, s, h);
+    }
+  };
   // the B operands of one 16-query step of a block: dO hi, dO lo, Q
   // columns for every 32-column block of the head dimension
   struct ColOps { bf16x8 dh[DB], dl[DB], q[DB]; };
@@ -195,18 +196,21 @@ void attn_bwd_dkv_kernel(
       c.q[b] = ld_colop<D>(sb->q, s2, 32 * b, lane);
     }
   };
+  // P, dS of one 16-query step as two-term bf16 splits (the A operands)
+  struct Packed { bf16x8 ph, pl, sh, sl; };
+  auto pack = [&](const f32x16 &pa, const f32x16 &ds, int s2, Packed &k) {
+    pack_split(pa, 8 * s2, k.ph, k.pl);
+    pack_split(ds, 8 * s2, k.sh, k.sl);
+  };
   // dV += P^T dO and dK += dS^T Q over one 16-query step
-  auto accum = [&](const f32x16 &pa, const f32x16 &ds, int s2, const ColOps &c) {
-    bf16x8 aph, apl, ash, asl;
-    pack_split(pa, 8 * s2, aph, apl);
-    pack_split(ds, 8 * s2, ash, asl);
+  auto accum = [&](const Packed &k, const ColOps &c) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      acc_dv[b] = mfma32(aph, c.dh[b], acc_dv[b]);
-      acc_dv[b] = mfma32(aph, c.dl[b], acc_dv[b]);
-      acc_dv[b] = mfma32(apl, c.dh[b], acc_dv[b]);
-      acc_dk[b] = mfma32(ash, c.q[b], acc_dk[b]);
-      acc_dk[b] = mfma32(asl, c.q[b], acc_dk[b]);
+      acc_dv[b] = mfma32(k.ph, c.dh[b], acc_dv[b]);
+      acc_dv[b] = mfma32(k.ph, c.dl[b], acc_dv[b]);
+      acc_dv[b] = mfma32(k.pl, c.dh[b], acc_dv[b]);
+      acc_dk[b] = mfma32(k.sh, c.q[b], acc_dk[b]);
+      acc_dk[b] = mfma32(k.sl, c.q[b], acc_dk[b]);
     }
   };
 
@@ -216,65 +220,75 @@ void attn_bwd_dkv_kernel(
   if (f >= nqb) {
     for (; qb < nqb; ++qb) {
       sync(qb);
-      issue(slot(qb + 3), qb);
+      issue(slot(qb + 4), qb);
     }
   } else {
     for (; qb < f - 1; ++qb) {
       sync(qb);
-      issue(slot(qb + 3), qb);
+      issue(slot(qb + 4), qb);
     }
     f32x16 sa, dp;
+    RowOps ro;
     sync(qb);
-    issue(slot(qb + 3), qb);
-    sdp(slot(f), sa, dp);
-    // One steady iteration (block qb; the slots are distinct, which the
+    issue(slot(qb + 4), qb);
+    rowops(slot(f), ro);
+    sa = zero16();
+    dp = zero16();
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      sa = mfma32(ro.q[s], kreg[s], sa);
+      dp = mfma32(ro.dh[s], vreg[s], dp);
+      dp = mfma32(ro.dl[s], vreg[s], dp);
+    }
+    rowops(slot(min(f + 1, nqb - 1)), ro);
+    // One steady iteration (block qb).  The slots are distinct, which the
     // restrict qualifiers state, so the compiler does not make LDS reads
     // wait for the global->LDS loads into `fill`; the explicit vmcnt before
-    // each barrier is what orders them).  One wavefront per SIMD: no other
-    // wavefront hides LDS latency or the exponentials, so the iteration is
-    // laid out by hand in fenced regions: (1) all row-operand reads of block
-    // qb + 1; (2) its S and dP MFMAs with block qb's exponentials between
-    // them, and the column operands of block qb's first query step; (3) that
-    // step's MFMAs with the second step's reads; (4) the second step's MFMAs.
-    // Block f (the diagonal) has the index mask; later blocks up to nqb - 2
-    // lie inside the range; block nqb - 1 goes through the tail below.
+    // each barrier is what orders them.  One wavefront per SIMD: no other
+    // wavefront hides LDS latency or the VALU work, so the iteration is laid
+    // out by hand in fenced regions: (1) S and dP MFMAs of block qb + 1 (row
+    // operands read last iteration) with block qb's exponentials and splits
+    // between them, and the column operands of its first query step; (2)
+    // that step's MFMAs with the second step's reads; (3) the second step's
+    // MFMAs with the row-operand reads of block qb + 2.  Block f (the
+    // diagonal) has the index mask; later blocks up to nqb - 2 lie inside
+    // the range; block nqb - 1 goes through the tail below.
     auto iter = [&](auto edge_tag, KvStage<D> *__restrict__ fill,
-                    const KvStage<D> *__restrict__ cur, const KvStage<D> *__restrict__ nxt) {
+                    const KvStage<D> *__restrict__ cur, const KvStage<D> *__restrict__ nx2) {
       issue(fill, qb);
-      bf16x8 ra[KSTEPS], rh[KSTEPS], rl[KSTEPS];
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        ra[s] = ld_rowop<D>(nxt->q, col, s, h);
-        rh[s] = ld_rowop<D>(nxt->dh, col, s, h);
-        rl[s] = ld_rowop<D>(nxt->dl, col, s, h);
-      }
-      __builtin_amdgcn_sched_barrier(0);
       f32x16 sn = zero16(), dn = zero16();
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        sn = mfma32(ra[s], kreg[s], sn);
-        dn = mfma32(rh[s], vreg[s], dn);
-        dn = mfma32(rl[s], vreg[s], dn);
+        sn = mfma32(ro.q[s], kreg[s], sn);
+        dn = mfma32(ro.dh[s], vreg[s], dn);
+        dn = mfma32(ro.dl[s], vreg[s], dn);
       }
       softmax(edge_tag, cur, qb, sa, dp);
+      Packed k0, k1;
+      pack(sa, dp, 0, k0);
+      pack(sa, dp, 1, k1);
       ColOps c0;
       colops(cur, 0, c0);
       __builtin_amdgcn_sched_barrier(0);
       ColOps c1;
       colops(cur, 1, c1);
-      accum(sa, dp, 0, c0);
+      accum(k0, c0);
       __builtin_amdgcn_sched_barrier(0);
-      accum(sa, dp, 1, c1);
+      rowops(nx2, ro);
+      accum(k1, c1);
+      // keeps the row-operand reads here, under the MFMAs (otherwise they
+      // sink to the top of the next iteration, where the MFMAs wait on them)
+      asm volatile("" ::: "memory");
       sa = sn;
       dp = dn;
     };
     qb = f;
     if (qb < nqb - 1) {
       sync(qb);
-      iter(std::true_type(), slot(qb + 3), slot(qb), slot(qb + 1));
+      iter(std::true_type(), slot(qb + 4), slot(qb), slot(min(qb + 2, nqb - 1)));
       for (++qb; qb < nqb - 1; ++qb) {
         sync(qb);
-        iter(std::false_type(), slot(qb + 3), slot(qb), slot(qb + 1));
+        iter(std::false_type(), slot(qb + 4), slot(qb), slot(min(qb + 2, nqb - 1)));
       }
     }
     sync(qb);   // qb == nqb - 1: nothing left to issue
@@ -282,8 +296,10 @@ void attn_bwd_dkv_kernel(
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       ColOps c;
+      Packed k;
       colops(slot(qb), s2, c);
-      accum(sa, dp, s2, c);
+      pack(sa, dp, s2, k);
+      accum(k, c);
     }
   }
 
@@ -304,7 +320,7 @@ void attn_bwd_dkv_kernel(
 constexpr int kQBQ = 128;      // queries per workgroup (32 per wavefront)
 constexpr int kQBK = 32;       // keys per block
 constexpr int kQThreads = 256;
-constexpr int kQStages = 4;    // LDS ring: two blocks in use, two loading
+constexpr int kQStages = 5;    // LDS ring: three blocks resident, two loading
 
 template <int D>
 struct QStage {
@@ -321,7 +337,7 @@ void attn_bwd_dq_kernel(
     const float *__restrict__ lse, const float *__restrict__ drow,
     const uint8_t *__restrict__ flags, float *__restrict__ dqs, int64_t S, int32_t BH,
     float scale) {
-  static_assert(kQStages == 4, "block kb + 3 is issued into the slot of block kb - 1");
+  static_assert(kQStages == 5, "block kb + 4 is issued into the slot of block kb - 1");
   extern __shared__ __align__(16) unsigned char smraw[];
   QStage<D> *stg = reinterpret_cast<QStage<D> *>(smraw);
   uint8_t *fl_lds = smraw + sizeof(QStage<D>) * kQStages;   // flags of keys 0 .. kend-1
@@ -333,7 +349,8 @@ void attn_bwd_dq_kernel(
   const int item = (int)blockIdx.x;
   const int qb = nqb - 1 - item / BH;             // heaviest first
   const int64_t bh = item % BH;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront index, scalar
   const int col = lane & 31, h = lane >> 5;
   const int64_t q0w = (int64_t)qb * kQBQ + w * 32;
   const int64_t q = q0w + col;
@@ -378,41 +395,28 @@ void attn_bwd_dq_kernel(
   // the loop (otherwise it re-waits for them inside every iteration)
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-  auto issue = [&](QStage<D> *st, int kb) {   // block kb + 3 into st
-    if (kb + 3 < nkb) {
-      tile_load<D, kQBK, kQThreads>(st->k, Kg, (int64_t)(kb + 3) * kQBK, S - 1, tid);
-      tile_load<D, kQBK, kQThreads>(st->v, Vg, (int64_t)(kb + 3) * kQBK, S - 1, tid);
+  auto issue = [&](QStage<D> *st, int kb) {   // block kb + 4 into st
+    if (kb + 4 < nkb) {
+      tile_load<D, kQBK, kQThreads>(st->k, Kg, (int64_t)(kb + 4) * kQBK, S - 1, tid);
+      tile_load<D, kQBK, kQThreads>(st->v, Vg, (int64_t)(kb + 4) * kQBK, S - 1, tid);
     }
   };
   auto slot = [&](int kb) { return &stg[(kb + kQStages) % kQStages]; };
-  for (int j = 0; j < 2; ++j) issue(slot(j), j - 3);
+  for (int j = 0; j < 3; ++j) issue(slot(j), j - 4);
   f32x16 acc_dq[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc_dq[b] = zero16();
 
-  // Iteration kb (-1 .. nkb - 1) waits for block kb + 1, has wavefront 0
-  // turn that block's flags into its bias slot, and issues block kb + 3 into
-  // the slot of block kb - 1.
+  // Iteration kb (-1 .. nkb - 1) waits for block kb + 2, has wavefront 0
+  // turn block kb + 1's flags into its bias slot, and issues block kb + 4
+  // into the slot of block kb - 1.
   auto sync = [&](int kb) {
-    if (kb + 2 >= nkb) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (kb + 3 >= nkb) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
     lds_barrier();
     if (w == 0 && lane < kQBK && kb + 1 < nkb) {
       const int64_t kk = (int64_t)(kb + 1) * kQBK + lane;
       slot(kb + 1)->bias[lane] = (kk < kend && !(fl_lds[kk] & LH_ROW_REDUNDANT)) ? 0.f : -INFINITY;
-    }
-  };
-  // S^T = K Q^T and dP^T = V dO^T of a block (lane: query column; rows:
-  // keys 8I + 4h + J)
-  auto sdp = [&](const QStage<D> *sb, f32x16 &sa, f32x16 &dp) {
-    sa = zero16();
-    dp = zero16();
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      sa = mfma32(ld_rowop<D>(sb->k, col, s, h), qreg[s], sa);
-      const bf16x8 av = ld_rowop<D>(sb->v, col, s, h);
-      dp = mfma32(av, dregh[s], dp);
-      dp = mfma32(av, dregl[s], dp);
     }
   };
   // dS^T of block kb from its S^T, dP^T (in place); EDGE: the block on the
@@ -434,15 +438,22 @@ void attn_bwd_dq_kernel(
       }
     }
   };
+  // the A operands of S^T and dP^T of a block: K and V rows
+  struct RowOps { bf16x8 k[KSTEPS], v[KSTEPS]; };
+  auto rowops = [&](const QStage<D> *sb, RowOps &r) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      r.k[s] = ld_rowop<D>(sb->k, col, s, h);
+      r.v[s] = ld_rowop<D>(sb->v, col, s, h);
+    }
+  };
   // the A operands of one 16-key step: K^T through the transposing read
   auto colops = [&](const QStage<D> *sb, int s2, bf16x8 (&a)[DB]) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) a[b] = ld_colop<D>(sb->k, s2, 32 * b, lane);
   };
-  // dQ^T += K^T dS^T over one 16-key step
-  auto accum = [&](const f32x16 &ds, int s2, const bf16x8 (&a)[DB]) {
-    bf16x8 bsh, bsl;
-    pack_split(ds, 8 * s2, bsh, bsl);
+  // dQ^T += K^T dS^T over one 16-key step (dS^T as a two-term bf16 split)
+  auto accum = [&](const bf16x8 &bsh, const bf16x8 &bsl, const bf16x8 (&a)[DB]) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       acc_dq[b] = mfma32(a[b], bsh, acc_dq[b]);
@@ -456,62 +467,72 @@ void attn_bwd_dq_kernel(
   if (lw < 0) {
     for (; kb < nkb; ++kb) {
       sync(kb);
-      issue(slot(kb + 3), kb);
+      issue(slot(kb + 4), kb);
     }
   } else {
     f32x16 sa, dp;
+    RowOps ro;
     sync(kb);
-    issue(slot(kb + 3), kb);
-    sdp(slot(0), sa, dp);
-    // steady iterations: S^T, dP^T of block kb + 1 in fenced regions with
-    // block kb's exponentials and dQ (one wavefront per SIMD, so the issue
-    // order is laid out by hand, as in the dK/dV kernel; the restrict
-    // qualifiers state that the slots are distinct)
-    auto iter = [&](QStage<D> *__restrict__ fill, const QStage<D> *__restrict__ cur,
-                    const QStage<D> *__restrict__ nxt) {
-      issue(fill, kb);
-      bf16x8 rk[KSTEPS], rv[KSTEPS];
+    issue(slot(kb + 4), kb);
+    rowops(slot(0), ro);
+    sa = zero16();
+    dp = zero16();
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        rk[s] = ld_rowop<D>(nxt->k, col, s, h);
-        rv[s] = ld_rowop<D>(nxt->v, col, s, h);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < KSTEPS; ++s) {
+      sa = mfma32(ro.k[s], qreg[s], sa);
+      dp = mfma32(ro.v[s], dregh[s], dp);
+      dp = mfma32(ro.v[s], dregl[s], dp);
+    }
+    rowops(slot(min(1, nkb - 1)), ro);
+    // steady iterations (block kb), laid out as in the dK/dV kernel: S^T,
+    // dP^T of block kb + 1 from row operands read last iteration, with block
+    // kb's exponentials and splits between them; then the dQ MFMAs, with
+    // block kb + 2's row-operand reads under the last ones.  The restrict
+    // qualifiers state that the slots are distinct.
+    auto iter = [&](QStage<D> *__restrict__ fill, const QStage<D> *__restrict__ cur,
+                    const QStage<D> *__restrict__ nx2) {
+      issue(fill, kb);
       f32x16 sn = zero16(), dn = zero16();
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        sn = mfma32(rk[s], qreg[s], sn);
-        dn = mfma32(rv[s], dregh[s], dn);
-        dn = mfma32(rv[s], dregl[s], dn);
+        sn = mfma32(ro.k[s], qreg[s], sn);
+        dn = mfma32(ro.v[s], dregh[s], dn);
+        dn = mfma32(ro.v[s], dregl[s], dn);
       }
       softmax(std::false_type(), cur, kb, sa, dp);
+      bf16x8 h0, l0, h1, l1;
+      pack_split(dp, 0, h0, l0);
+      pack_split(dp, 8, h1, l1);
       bf16x8 a0[DB];
       colops(cur, 0, a0);
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 a1[DB];
       colops(cur, 1, a1);
-      accum(dp, 0, a0);
+      accum(h0, l0, a0);
       __builtin_amdgcn_sched_barrier(0);
-      accum(dp, 1, a1);
+      rowops(nx2, ro);
+      accum(h1, l1, a1);
+      asm volatile("" ::: "memory");   // keeps the row-operand reads under the MFMAs
       sa = sn;
       dp = dn;
     };
     for (kb = 0; kb < lw; ++kb) {
       sync(kb);
-      iter(slot(kb + 3), slot(kb), slot(kb + 1));
+      iter(slot(kb + 4), slot(kb), slot(min(kb + 2, nkb - 1)));
     }
     sync(kb);   // kb == lw: the diagonal block
-    issue(slot(kb + 3), kb);
+    issue(slot(kb + 4), kb);
     softmax(std::true_type(), slot(kb), kb, sa, dp);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 a[DB];
+      bf16x8 a[DB], bh_, bl_;
       colops(slot(kb), s2, a);
-      accum(dp, s2, a);
+      pack_split(dp, 8 * s2, bh_, bl_);
+      accum(bh_, bl_, a);
     }
     for (++kb; kb < nkb; ++kb) {
       sync(kb);
-      issue(slot(kb + 3), kb);
+      issue(slot(kb + 4), kb);
     }
   }
 
