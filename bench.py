@@ -118,6 +118,43 @@ def cpu_baseline(w, Q, K, V, dO):
                       f"(NumPy float64), rate scaled to all {w.H} heads"}
 
 
+def measured_peaks(torch, dev):
+    """The ceilings this device sustains, measured beside the published
+    peaks: HBM by one device copy of 1 GiB (reads and writes 1 GiB each),
+    bf16 MFMA by the library's probe (independent chains of the MFMA the
+    attention kernels use, no memory traffic)."""
+    import ctypes as C
+    from sparse_long_context_amd import _lib
+
+    st = torch.cuda.current_stream()
+    n = 1 << 28
+    a, b = torch.ones(n, device=dev), torch.empty(n, device=dev)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record(st)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(st)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * 4 * n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, b
+    blocks, iters = 256 * 8, 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    fn = _lib.lib().lh_probe_mfma_bf16
+    sp = C.c_void_p(st.cuda_stream)
+    _lib.check(fn(blocks, 10, C.c_void_p(out.data_ptr()), sp), "lh_probe_mfma_bf16")
+    e0.record(st)
+    _lib.check(fn(blocks, iters, C.c_void_p(out.data_ptr()), sp), "lh_probe_mfma_bf16")
+    e1.record(st)
+    torch.cuda.synchronize()
+    flops = blocks * 4 * 8 * iters * 32768.0
+    mfma_tf = flops / (e0.elapsed_time(e1) / 1e3) / 1e12
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "mfma_bf16_TFLOPs": round(mfma_tf, 1),
+            "how": "one 1 GiB device copy (read+write); lh_probe_mfma_bf16, 2048 workgroups x "
+                   "2000 rounds of 8 independent 32x32x16 bf16 MFMAs per wavefront"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -170,6 +207,9 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     value = w.B * w.N / (ms / 1e3)
     print(f"[bench] layer fwd+bwd {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    peaks = measured_peaks(torch, dev)
+    print(f"[bench] measured ceilings {peaks}", file=sys.stderr, flush=True)
 
     stages, roof = None, None
     if not args.no_stages and w.dtype == "bf16":
@@ -225,6 +265,7 @@ def main():
         roof = {"kernel": KERNEL_OF[name], "bound": "mfma", "achieved": round(ach, 2),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "avg_launch_ms": round(stages[name]["ms"], 4),
+                "frac_of_measured_peak": round(ach / peaks["mfma_bf16_TFLOPs"], 4),
                 "algorithmic_per_launch": work[name]}
         for n, e in stages.items():
             print(f"[bench] stage {n:20s} {e}", file=sys.stderr, flush=True)
@@ -240,7 +281,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "N": w.N, "H": w.H, "d": w.d, "p": w.p,
                    "L": w.L, "S": S, "K": w.K, "io_dtype": w.dtype, "out_dtype": w.dtype},
-        "roofline": roof, "cpu_baseline": cpu, "stages": stages,
+        "roofline": roof, "cpu_baseline": cpu, "measured_peaks": peaks, "stages": stages,
     }
     print(json.dumps(line))
 

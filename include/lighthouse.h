@@ -300,6 +300,19 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *saved,
                        const void *dout, void *dq, void *dk, void *dv,
                        void *ws, size_t ws_bytes, lh_stream stream);
 
+/* ---- measurement helper (not part of the layer) ----
+ * Runs `blocks` workgroups of 256 threads, each wavefront issuing `iters`
+ * rounds of 8 independent v_mfma_f32_32x32x16_bf16 (the MFMA the attention
+ * kernels use), so one launch performs blocks * 4 * 8 * iters * 32768 flops
+ * with no memory traffic.  Timing a launch gives the bf16 MFMA rate the
+ * device sustains, the achievable ceiling beside the published peak.
+ * out: device float32 [blocks * 256], caller-owned, overwritten with a
+ * checksum.  Errors: LH_ERR_INVALID_ARG for blocks outside 1 .. 2^31-1,
+ * iters <= 0 or a NULL out (nothing launched); LH_ERR_HIP after a failed
+ * launch.  Asynchronous on `stream`. */
+lh_status lh_probe_mfma_bf16(int64_t blocks, int32_t iters, float *out,
+                             lh_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

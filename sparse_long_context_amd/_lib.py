@@ -67,7 +67,8 @@ _PROTOS = {
     "lh_layer_fwd": [_P] * 4 + [C.POINTER(Saved), _P, C.c_size_t, _P],
     "lh_layer_bwd": [C.POINTER(Saved)] + [_P] * 4 + [_P, C.c_size_t, _P],
 }
-EXPORTS = ["lh_validate", "lh_get_sizes", "lh_status_string", "lh_version", *_PROTOS]
+EXPORTS = ["lh_validate", "lh_get_sizes", "lh_status_string", "lh_version", "lh_probe_mfma_bf16",
+           *_PROTOS]
 
 _lib = None
 _lock = threading.Lock()
@@ -90,6 +91,8 @@ def lib():
             L.lh_status_string.restype = C.c_char_p
             L.lh_version.argtypes = []
             L.lh_version.restype = C.c_char_p
+            L.lh_probe_mfma_bf16.argtypes = [C.c_int64, C.c_int32, _P, _P]
+            L.lh_probe_mfma_bf16.restype = C.c_int32
             for name, args in _PROTOS.items():
                 fn = getattr(L, name)
                 fn.argtypes = [_PD] + args

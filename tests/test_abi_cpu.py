@@ -124,3 +124,11 @@ def test_stage_calls_reject_bad_args_without_launch(lib):
 def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -99):
         assert len(lib.lh_status_string(s)) > 0
+
+
+def test_mfma_probe_rejects_bad_args_without_launch(lib):
+    buf = C.c_void_p(0x1000)   # never dereferenced: every case fails validation first
+    for blocks, iters, out in ((0, 10, buf), (-1, 10, buf), (1 << 31, 10, buf), (8, 0, buf),
+                               (8, 10, None)):
+        st = lib.lh_probe_mfma_bf16(blocks, iters, out, None)
+        assert st == L.LH_ERR_INVALID_ARG, (blocks, iters, out, st)
