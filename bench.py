@@ -8,11 +8,13 @@ adjoints).  Inputs are resident in HBM before the timed region starts.
 Prints ONE JSON line.  Besides the headline (tokens/s of fwd+bwd), it reports
 per-stage times with algorithmic GB/s or TFLOP/s (stage mode: every stage
 entry point timed alone with HIP events on the stream its kernels run on),
-a roofline object for the dominant kernel, and the CPU oracle timed on a
-bounded sample of the same workload.
+a roofline object for the dominant kernel, the device's measured HBM-copy
+and MFMA ceilings, dense causal attention over all N tokens (torch's fused
+SDPA) as the comparison point, and the CPU oracle timed on a bounded sample
+of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 4]
-                       [--no-cpu] [--no-stages]
+                       [--no-cpu] [--no-stages] [--no-dense]
 """
 from __future__ import annotations
 
@@ -41,6 +43,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense causal SDPA comparison (about 1 s at the 128K workload)")
     ap.add_argument("--stage-reps", type=int, default=10)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known byte "
@@ -153,6 +157,37 @@ def measured_peaks(torch, dev):
     return {"hbm_copy_GBps": round(copy_gbs, 1), "mfma_bf16_TFLOPs": round(mfma_tf, 1),
             "how": "one 1 GiB device copy (read+write); lh_probe_mfma_bf16, 2048 workgroups x "
                    "2000 rounds of 8 independent 32x32x16 bf16 MFMAs per wavefront"}
+
+
+def dense_sdpa(torch, Q, K, V, dO, reps=2):
+    """The pages' comparison point: dense causal attention over all N tokens
+    (torch's fused SDPA kernels; the unfused math path is never used), forward
+    and backward on the same inputs.  Returns the faster fused backend."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    best = None
+    for backend in (SDPBackend.EFFICIENT_ATTENTION, SDPBackend.FLASH_ATTENTION):
+        try:
+            q, k, v = (x.detach().clone().requires_grad_(True) for x in (Q, K, V))
+            with sdpa_kernel([backend]):
+                def run():
+                    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+                    o.backward(dO)
+                run()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    run()
+                e1.record()
+                torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            if best is None or ms < best[1]:
+                best = (backend.name, ms)
+            del q, k, v
+        except RuntimeError as ex:
+            print(f"[bench] dense SDPA {backend.name} unavailable: {ex}", file=sys.stderr, flush=True)
+    return best
 
 
 def main():
@@ -270,6 +305,17 @@ def main():
         for n, e in stages.items():
             print(f"[bench] stage {n:20s} {e}", file=sys.stderr, flush=True)
 
+    dense = None
+    if not args.no_dense and w.dtype == "bf16":
+        best = dense_sdpa(torch, Q, K, V, dO)
+        if best:
+            dense = {"backend": best[0], "ms_per_step": round(best[1], 3),
+                     "tokens_per_s": round(w.B * w.N / (best[1] / 1e3), 1),
+                     "lighthouse_speedup": round(best[1] / ms, 2),
+                     "what": "dense causal attention over all N tokens, forward+backward, "
+                             "torch fused SDPA on the same inputs"}
+            print(f"[bench] dense SDPA {dense}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, Qc, Kc, Vc, dOc.to(out))
@@ -281,7 +327,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "N": w.N, "H": w.H, "d": w.d, "p": w.p,
                    "L": w.L, "S": S, "K": w.K, "io_dtype": w.dtype, "out_dtype": w.dtype},
-        "roofline": roof, "cpu_baseline": cpu, "measured_peaks": peaks, "stages": stages,
+        "roofline": roof, "cpu_baseline": cpu, "measured_peaks": peaks, "dense_sdpa": dense,
+        "stages": stages,
     }
     print(json.dumps(line))
 
