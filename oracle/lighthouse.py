@@ -36,7 +36,7 @@ Notation (one batch element b, one head h):
   subsequence length S = K + n_c.
 
 Parity pins for every function live in tests/test_oracle_*.py.  Conventions
-R-5, R-7, R-9, R-11, R-12 and R-14 are readings of open points: they are
+R-5, R-7, R-9, R-11, R-12, R-14 and R-14' are readings of open points: they are
 pinned by invariants and special cases, not by a value the pages print
 ("parity unpinned" by the pages themselves).
 """
@@ -436,6 +436,43 @@ def scatter_adjoint(dO, sel: Selection, N: int):
 
 
 # --------------------------------------------------------------------------
+# O8'  span-broadcast scatter: the other reading of [EXP-2C]'s scatter-back,
+#      where an output is put back over the whole span of its entry
+# --------------------------------------------------------------------------
+def span_owner(sel: Selection, g: Geometry):
+    """R-14' (span broadcast): for each token t the row of the finest
+    selected entry whose span [i*p**l, (i+1)*p**l) contains t.  The stratum
+    root is always selected, so every token has one; a REDUNDANT entry never
+    owns a token, since finer selected entries cover its whole span.  Inside
+    a span this is acausal (a token sees the summary of later tokens), which
+    is the pages' own caveat about decoding; across coarsest cells it is
+    causal."""
+    t = np.arange(g.N)
+    own = np.full(g.N, -1)
+    for l in range(g.L - 1, -1, -1):          # coarse to fine: finer entries win
+        r = sel.row_of[g.level_offsets[l] + t // g.p ** l]
+        own = np.where(r >= 0, r, own)
+    return own
+
+
+def scatter_span(OS, sel: Selection, g: Geometry):
+    """O[t] = OS[span_owner(t)]."""
+    OS = np.asarray(OS, np.float64)
+    return OS[span_owner(sel, g)]
+
+
+def scatter_span_adjoint(dO, sel: Selection, g: Geometry):
+    """dOS[j] = sum of dO[t] over the tokens t that row j owns, in token
+    order; zero for rows that own no token."""
+    dO = np.asarray(dO, np.float64)
+    dOS = np.zeros((len(sel.sel_idx), dO.shape[1]))
+    own = span_owner(sel, g)
+    for t in range(g.N):
+        dOS[own[t]] += dO[t]
+    return dOS
+
+
+# --------------------------------------------------------------------------
 # O11, O12  gather adjoint and pooling adjoint
 # --------------------------------------------------------------------------
 def gather_adjoint(dXS, sel: Selection, g: Geometry):
@@ -482,12 +519,16 @@ class HeadForward:
     OS: np.ndarray
     LSE: np.ndarray
     O: np.ndarray
+    scatter_mode: str = "hold"
 
 
-def head_forward(Q, K_, V, g: Geometry, scale=None, store=None, selection=None):
+def head_forward(Q, K_, V, g: Geometry, scale=None, store=None, selection=None,
+                 scatter_mode="hold"):
     """One head of the layer: pyramid -> scores -> selection -> gather ->
     attention -> scatter.  `selection` (a Selection) replaces the computed
-    one, so downstream stages can be checked on a given selection."""
+    one, so downstream stages can be checked on a given selection.
+    scatter_mode: "hold" (R-14, causal hold) or "span" (R-14', span
+    broadcast)."""
     g.check()
     d = np.asarray(Q).shape[1]
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
@@ -497,8 +538,14 @@ def head_forward(Q, K_, V, g: Geometry, scale=None, store=None, selection=None):
     Ql, Kl, Vl = (pyramid(X, g, store) for X in (Q, K_, V))
     QS, KS, VS = gather(Ql, sel.sel_idx), gather(Kl, sel.sel_idx), gather(Vl, sel.sel_idx)
     OS, LSE = attention_fwd(QS, KS, VS, sel.sel_flags, scale)
-    O = scatter(OS, sel, g.N)
-    return HeadForward(g, scale, sQ, sK, sig, sel, Ql, Kl, Vl, QS, KS, VS, OS, LSE, O)
+    if scatter_mode == "hold":
+        O = scatter(OS, sel, g.N)
+    elif scatter_mode == "span":
+        O = scatter_span(OS, sel, g)
+    else:
+        raise ValueError(f"scatter_mode {scatter_mode!r}")
+    return HeadForward(g, scale, sQ, sK, sig, sel, Ql, Kl, Vl, QS, KS, VS, OS, LSE, O,
+                       scatter_mode)
 
 
 def head_backward(fw: HeadForward, dO):
@@ -506,7 +553,10 @@ def head_backward(fw: HeadForward, dO):
     attention backward -> gather adjoint -> pooling adjoint.  Nothing flows
     through the scores or the selection [EXP-2B], [NEWS]."""
     g = fw.g
-    dOS = scatter_adjoint(dO, fw.sel, g.N)
+    if fw.scatter_mode == "span":
+        dOS = scatter_span_adjoint(dO, fw.sel, g)
+    else:
+        dOS = scatter_adjoint(dO, fw.sel, g.N)
     dQS, dKS, dVS = attention_bwd(fw.QS, fw.KS, fw.VS, fw.sel.sel_flags, fw.scale, dOS)
     out = []
     for dXS in (dQS, dKS, dVS):
@@ -514,10 +564,11 @@ def head_backward(fw: HeadForward, dO):
     return tuple(out) + (dOS, dQS, dKS, dVS)
 
 
-def layer_forward(Q, K_, V, p, L, K, scale=None, store=None):
+def layer_forward(Q, K_, V, p, L, K, scale=None, store=None, scatter_mode="hold"):
     """[B, H, N, d] arrays -> list over (b, h) of HeadForward."""
     Q = np.asarray(Q)
     B, H, N, _ = Q.shape
     g = Geometry(N, p, L, K).check()
-    return [[head_forward(Q[b, h], K_[b, h], V[b, h], g, scale, store)
+    return [[head_forward(Q[b, h], K_[b, h], V[b, h], g, scale, store,
+                          scatter_mode=scatter_mode)
              for h in range(H)] for b in range(B)]

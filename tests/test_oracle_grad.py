@@ -1,7 +1,7 @@
 """Pins of the oracle's hand-written backward.
 
 (1) central finite differences in float64 on tiny inputs, with the
-    selection checked unchanged at +-h;
+    selection checked unchanged at +-h (both scatter modes);
 (2) autograd through an independent plain-torch float64 forward of the
     layer on the same selection (pooling by avg_pool1d over whole spans,
     index_select gathers, a masked softmax, and a hold map built with a
@@ -19,11 +19,12 @@ def rnd(shape, seed):
     return np.random.default_rng(seed).standard_normal(shape)
 
 
-def test_finite_differences():
+@pytest.mark.parametrize("mode", ["hold", "span"])
+def test_finite_differences(mode):
     N, p, L, d, ks = 32, 2, 3, 4, 3
     g = orc.Geometry(N, p, L, ks * (N // 4)).check()
     Q, K, V, dO = (rnd((N, d), s) for s in (1, 2, 3, 4))
-    fw = orc.head_forward(Q, K, V, g)
+    fw = orc.head_forward(Q, K, V, g, scatter_mode=mode)
     dQ, dK, dV = orc.head_backward(fw, dO)[:3]
     h = 1e-6
     X = [Q, K, V]
@@ -34,7 +35,7 @@ def test_finite_differences():
                 for sgn in (1, -1):
                     Xs = [x.copy() for x in X]
                     Xs[which][t, c] += sgn * h
-                    f2 = orc.head_forward(*Xs, g)
+                    f2 = orc.head_forward(*Xs, g, scatter_mode=mode)
                     assert np.array_equal(f2.sel.sel_idx, fw.sel.sel_idx)
                     outs.append(np.sum(f2.O * dO))
                 fd = (outs[0] - outs[1]) / (2 * h)

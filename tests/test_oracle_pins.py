@@ -146,6 +146,12 @@ def test_golden_hand_selection_tie():
     assert list(sel.near_tie) == gd["expect_near_tie_K_tie"]
 
 
+def test_golden_hand_span_owner():
+    for K, key in ((6, "expect_span_owner"), (4, "expect_span_owner_K_tie")):
+        gd, g, s = _sel_from_golden(K)
+        assert list(orc.span_owner(orc.select(s, g), g)) == gd[key]
+
+
 # ---------------------------------------------------------------- O3-O5 selection
 def _selection_case(N, p, L, ks, seed, ties=False):
     g = orc.Geometry(N, p, L, ks * (N // p ** (L - 1))).check()
@@ -235,6 +241,26 @@ def test_hold_source_brute_force():
         assert src[t] == (max(c, key=lambda j: sel.sel_anchor[j]) if c else -1)
 
 
+@pytest.mark.parametrize("N,p,L,ks", [(1024, 4, 4, 13), (512, 2, 5, 9), (512, 8, 3, 30)])
+def test_span_owner_brute_force(N, p, L, ks):
+    """Every token's owner is the finest selected entry whose span holds it,
+    found by scanning every selected row's span; the owners are exactly the
+    non-redundant rows (a non-redundant row keeps an uncovered token)."""
+    g, s, sel = _selection_case(N, p, L, ks, 35, ties=True)
+    own = orc.span_owner(sel, g)
+    best = np.full(g.N, -1)
+    best_lev = np.full(g.N, 99)
+    for j, f in enumerate(sel.sel_idx):
+        lev, i = orc.entry_of_flat(g, f)
+        lo, hi = i * p ** lev, (i + 1) * p ** lev
+        for t in range(lo, hi):
+            if lev < best_lev[t]:
+                best[t], best_lev[t] = j, lev
+    assert np.array_equal(own, best)
+    nonred = {j for j in range(g.S) if not sel.sel_flags[j] & orc.FLAG_REDUNDANT}
+    assert set(own.tolist()) == nonred
+
+
 # ---------------------------------------------------------------- O6-O8 special cases
 def torch_causal_sdpa(Q, K, V):
     q, k, v = (torch.from_numpy(np.ascontiguousarray(x))[None, None] for x in (Q, K, V))
@@ -246,10 +272,11 @@ def torch_causal_sdpa(Q, K, V):
     (128, 4, 2, 4),      # L = 2, k_s = p
     (96, 3, 1, 0),       # L = 1: every token is its own coarsest entry
     (256, 4, 3, 20)])
-def test_full_selection_is_dense_causal_sdpa(N, p, L, ks):
+@pytest.mark.parametrize("mode", ["hold", "span"])
+def test_full_selection_is_dense_causal_sdpa(N, p, L, ks, mode):
     g = orc.Geometry(N, p, L, ks * (N // p ** (L - 1))).check()
     Q, K, V = rnd((N, 8), 1), rnd((N, 8), 2), rnd((N, 8), 3)
-    fw = orc.head_forward(Q, K, V, g)
+    fw = orc.head_forward(Q, K, V, g, scatter_mode=mode)
     np.testing.assert_allclose(fw.O, torch_causal_sdpa(Q, K, V), rtol=0, atol=1e-12)
 
 
@@ -267,6 +294,18 @@ def test_coarsest_only_closed_form(N, p, L):
     for t in range(Bc - 1, N):
         want[t] = OS[(t + 1) // Bc - 1]
     np.testing.assert_allclose(fw.O, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("N,p,L", [(256, 4, 3), (512, 2, 5)])
+def test_coarsest_only_closed_form_span(N, p, L):
+    """K = 0, span broadcast: every token of coarsest cell m takes row m."""
+    g = orc.Geometry(N, p, L, 0).check()
+    Q, K, V = rnd((N, 8), 4), rnd((N, 8), 5), rnd((N, 8), 6)
+    fw = orc.head_forward(Q, K, V, g, scatter_mode="span")
+    Bc = g.Bc
+    blk = lambda X: X.reshape(N // Bc, Bc, -1).mean(axis=1)
+    OS = torch_causal_sdpa(blk(Q), blk(K), blk(V))
+    np.testing.assert_allclose(fw.O, np.repeat(OS, Bc, axis=0), rtol=0, atol=1e-12)
 
 
 def test_softmax_rows_nonempty_and_normalised():
@@ -297,18 +336,19 @@ def test_token_causality_with_selection_fixed():
         assert np.array_equal(pert.O[:t + 1], base.O[:t + 1])
 
 
-def test_block_causality_unconditional():
+@pytest.mark.parametrize("mode", ["hold", "span"])
+def test_block_causality_unconditional(mode):
     N, p, L, ks = 512, 4, 4, 20
     g = orc.Geometry(N, p, L, ks * (N // 64)).check()
     Q, K, V = rnd((N, 8), 1), rnd((N, 8), 2), rnd((N, 8), 3)
-    base = orc.head_forward(Q, K, V, g)
+    base = orc.head_forward(Q, K, V, g, scatter_mode=mode)
     for m in (1, 3, 7):
         b = m * g.Bc
         Q2, K2, V2 = Q.copy(), K.copy(), V.copy()
         Q2[b:] = rnd(Q2[b:].shape, 50 + m) * 9
         K2[b:] = rnd(K2[b:].shape, 60 + m) * 9
         V2[b:] = rnd(V2[b:].shape, 70 + m)
-        pert = orc.head_forward(Q2, K2, V2, g)
+        pert = orc.head_forward(Q2, K2, V2, g, scatter_mode=mode)
         r = m * (ks + 1)
         assert np.array_equal(pert.sel.sel_idx[:r], base.sel.sel_idx[:r])
         assert np.array_equal(pert.O[:b], base.O[:b])
@@ -320,6 +360,14 @@ def test_scatter_adjoint_dot_product():
     x, y = rnd((g.S, 6), 1), rnd((g.N, 6), 2)
     lhs = np.sum(orc.scatter(x, sel, g.N) * y)
     rhs = np.sum(x * orc.scatter_adjoint(y, sel, g.N))
+    assert abs(lhs - rhs) < 1e-10 * (1 + abs(lhs))
+
+
+def test_scatter_span_adjoint_dot_product():
+    g, s, sel = _selection_case(1024, 4, 4, 13, 42, ties=True)
+    x, y = rnd((g.S, 6), 3), rnd((g.N, 6), 4)
+    lhs = np.sum(orc.scatter_span(x, sel, g) * y)
+    rhs = np.sum(x * orc.scatter_span_adjoint(y, sel, g))
     assert abs(lhs - rhs) < 1e-10 * (1 + abs(lhs))
 
 
