@@ -70,6 +70,15 @@ typedef int32_t lh_status;
 #define LH_ROW_LEADER    2u  /* finest row at its anchor: owns the outputs of
                                 tokens [anchor, next leader's anchor)       */
 
+/* lh_dims.scatter_mode: how subsequence outputs go back to token positions
+ * (explainer 2.C: a deterministic scatter puts each output back at its
+ * positions; the pages leave open which positions a coarse output covers) */
+#define LH_SCATTER_HOLD 0    /* causal hold: token t takes the leader with the
+                                largest anchor <= t (0 before the first)    */
+#define LH_SCATTER_SPAN 1    /* span broadcast: token t takes the finest
+                                selected entry whose span holds t (acausal
+                                inside a span, causal across coarsest cells) */
+
 typedef void *lh_stream;     /* a hipStream_t */
 
 /* Problem statement of one layer call (explainer section 2.A-2.C: sequence
@@ -78,7 +87,8 @@ typedef void *lh_stream;     /* a hipStream_t */
  *   B >= 1, H >= 1, N >= 1, p >= 2, L >= 1, N % p^(L-1) == 0,
  *   K >= 0, K % n_c == 0, K / n_c <= T - 1, S == K + n_c,
  *   E < 2^31, d in {64, 128}, io_dtype/out_dtype in {LH_F32, LH_BF16},
- *   out_dtype == LH_F32 when io_dtype == LH_F32, scale >= 0 and finite. */
+ *   out_dtype == LH_F32 when io_dtype == LH_F32, scale >= 0 and finite,
+ *   scatter_mode in {LH_SCATTER_HOLD, LH_SCATTER_SPAN}. */
 typedef struct lh_dims {
   int64_t B;
   int64_t N;
@@ -91,7 +101,7 @@ typedef struct lh_dims {
   int32_t io_dtype;   /* Q, K, V, dO, pyramid and subsequence rows           */
   int32_t out_dtype;  /* O, OS, dQ, dK, dV                                   */
   float scale;        /* softmax scale; 0 selects 1/sqrt(d)                  */
-  int32_t reserved;   /* must be 0                                           */
+  int32_t scatter_mode; /* LH_SCATTER_HOLD (0) or LH_SCATTER_SPAN (1)        */
 } lh_dims;
 
 /* Buffers the forward fills and the backward reads (all caller-owned).
@@ -143,6 +153,7 @@ typedef struct lh_sizes {
   size_t ws_attn_bwd;       /* workspace of lh_subseq_attn_bwd */
   size_t ws_layer_fwd;      /* workspace of lh_layer_fwd       */
   size_t ws_layer_bwd;      /* workspace of lh_layer_bwd       */
+  size_t owner_bytes;       /* span owner map [B,H,N] int32    */
 } lh_sizes;
 
 /* Host only (no HIP call).  LH_OK if `dims` satisfies every constraint
@@ -275,6 +286,24 @@ lh_status lh_scatter_bwd(const lh_dims *dims, const void *dout,
                          const int32_t *sel_anchor, const uint8_t *sel_flags,
                          float *dos, lh_stream stream);
 
+/* ---- stage 4, span broadcast (lh_dims.scatter_mode == LH_SCATTER_SPAN) ----
+ * lh_span_owner: owner[b,h,t] = the row of the finest selected entry whose
+ * span holds token t, from row_of [B,H,E]; out: owner [B,H,N] int32.
+ * lh_scatter_span: o[t] = os[owner[t]]; os [B,H,S,d] float32, o [B,H,N,d]
+ * out_dtype.
+ * lh_scatter_span_bwd: adjoint: dos[j] = sum of dout[t] over the tokens t
+ * of row j's span with owner[t] == j, in token order (zero for REDUNDANT
+ * rows, which own nothing); dout [B,H,N,d] out_dtype, sel_idx and
+ * sel_flags as the selection wrote them; out: dos [B,H,S,d] float32.
+ * These three ignore dims->scatter_mode. */
+lh_status lh_span_owner(const lh_dims *dims, const int32_t *row_of, int32_t *owner,
+                        lh_stream stream);
+lh_status lh_scatter_span(const lh_dims *dims, const float *os, const int32_t *owner,
+                          void *o, lh_stream stream);
+lh_status lh_scatter_span_bwd(const lh_dims *dims, const void *dout,
+                              const int32_t *sel_idx, const uint8_t *sel_flags,
+                              const int32_t *owner, float *dos, lh_stream stream);
+
 /* Adjoint of gather and pooling (explainer 2.B: gradients reach W_Q, W_K,
  * W_V through gather, attention and scatter only; the selection carries
  * none):  dx[t] = sum_l dxs[row_of(l, t / p^l)] / p^l over the selected
@@ -287,8 +316,10 @@ lh_status lh_gather_bwd(const lh_dims *dims, const float *dqs,
 
 /* ---- whole layer ----
  * Forward: pyramid+score, select, gather (+ transposed copies), attention,
- * scatter.  Fills every buffer of *saved and o [B,H,N,d] out_dtype.
- * Workspace: sizes.ws_layer_fwd bytes (may be 0 / NULL when that is 0). */
+ * scatter (causal hold, or span broadcast per dims->scatter_mode).  Fills
+ * every buffer of *saved and o [B,H,N,d] out_dtype.
+ * Workspace: sizes.ws_layer_fwd bytes (may be 0 / NULL when that is 0; the
+ * span owner map in span mode). */
 lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k,
                        const void *v, void *o, const lh_saved *saved,
                        void *ws, size_t ws_bytes, lh_stream stream);

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "liblighthouse.so")
 LH_OK, LH_ERR_INVALID_ARG, LH_ERR_UNSUPPORTED, LH_ERR_WORKSPACE, LH_ERR_HIP = 0, -1, -2, -3, -4
 LH_F32, LH_BF16 = 0, 1
 LH_ROW_REDUNDANT, LH_ROW_LEADER = 1, 2
+LH_SCATTER_HOLD, LH_SCATTER_SPAN = 0, 1
 
 
 class LighthouseError(RuntimeError):
@@ -28,7 +29,7 @@ class Dims(C.Structure):
     _fields_ = [("B", C.c_int64), ("N", C.c_int64), ("H", C.c_int32), ("d", C.c_int32),
                 ("p", C.c_int32), ("L", C.c_int32), ("K", C.c_int64), ("S", C.c_int64),
                 ("io_dtype", C.c_int32), ("out_dtype", C.c_int32), ("scale", C.c_float),
-                ("reserved", C.c_int32)]
+                ("scatter_mode", C.c_int32)]
 
 
 class Saved(C.Structure):
@@ -43,7 +44,7 @@ class Sizes(C.Structure):
                     "pyramid_bytes", "score_bytes", "row_i32_bytes", "row_u8_bytes",
                     "row_of_bytes", "subseq_bytes", "os_bytes", "lse_bytes", "token_io_bytes",
                     "token_out_bytes", "ws_attn_fwd", "ws_attn_bwd", "ws_layer_fwd",
-                    "ws_layer_bwd")]
+                    "ws_layer_bwd", "owner_bytes")]
 
 
 _P = C.c_void_p
@@ -64,6 +65,9 @@ _PROTOS = {
     "lh_scatter": [_P] * 4 + [_P],
     "lh_scatter_bwd": [_P] * 4 + [_P],
     "lh_gather_bwd": [_P] * 7 + [_P],
+    "lh_span_owner": [_P] * 2 + [_P],
+    "lh_scatter_span": [_P] * 3 + [_P],
+    "lh_scatter_span_bwd": [_P] * 5 + [_P],
     "lh_layer_fwd": [_P] * 4 + [C.POINTER(Saved), _P, C.c_size_t, _P],
     "lh_layer_bwd": [C.POINTER(Saved)] + [_P] * 4 + [_P, C.c_size_t, _P],
 }
@@ -113,9 +117,10 @@ def check(status: int, what: str):
         raise LighthouseError(status, what)
 
 
-def make_dims(B, N, H, d, p, L, K, S, io_dtype=LH_BF16, out_dtype=None, scale=0.0) -> Dims:
+def make_dims(B, N, H, d, p, L, K, S, io_dtype=LH_BF16, out_dtype=None, scale=0.0,
+              scatter_mode=LH_SCATTER_HOLD) -> Dims:
     return Dims(B, N, H, d, p, L, K, S, io_dtype, io_dtype if out_dtype is None else out_dtype,
-                float(scale), 0)
+                float(scale), int(scatter_mode))
 
 
 def sizes(dims: Dims) -> Sizes:

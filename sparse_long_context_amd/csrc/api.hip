@@ -20,7 +20,8 @@ lh_status make_geo(const lh_dims *dm, Geo *g) {
   memset(g, 0, sizeof(*g));
   if (dm->B < 1 || dm->H < 1 || dm->N < 1 || dm->p < 2 || dm->L < 1 || dm->d < 1)
     return LH_ERR_INVALID_ARG;
-  if (dm->reserved != 0) return LH_ERR_INVALID_ARG;
+  if (dm->scatter_mode != LH_SCATTER_HOLD && dm->scatter_mode != LH_SCATTER_SPAN)
+    return LH_ERR_INVALID_ARG;
   if (dm->L >= kMaxLevels) return LH_ERR_UNSUPPORTED;
   if (!(dm->scale >= 0.0f) || !isfinite(dm->scale)) return LH_ERR_INVALID_ARG;
   if ((dm->io_dtype != LH_F32 && dm->io_dtype != LH_BF16) ||
@@ -29,6 +30,7 @@ lh_status make_geo(const lh_dims *dm, Geo *g) {
   const int64_t lim = (int64_t)1 << 40;
   g->B = dm->B; g->N = dm->N; g->H = dm->H; g->d = dm->d; g->p = dm->p; g->L = dm->L;
   g->K = dm->K; g->S = dm->S; g->io = dm->io_dtype; g->out = dm->out_dtype;
+  g->mode = dm->scatter_mode;
   g->pw[0] = 1;
   for (int l = 1; l <= g->L; ++l)
     if (!mul_ok(g->pw[l - 1], g->p, lim, &g->pw[l])) return LH_ERR_INVALID_ARG;
@@ -83,11 +85,16 @@ static size_t ws_attn_bwd(const Geo &g) {
   if (g.io == LH_F32) return al256(z.drow);
   return 2 * al256(rows_bf16(g)) + al256(z.drow);        // dos split (hi, lo), drow
 }
+static size_t owner_bytes(const Geo &g) { return (size_t)g.BH() * g.N * 4; }
+static size_t ws_layer_fwd(const Geo &g) {
+  return g.mode == LH_SCATTER_SPAN ? al256(owner_bytes(g)) : 0;   // span owner map
+}
 static size_t ws_layer_bwd(const Geo &g) {
   Sizes z = sizes_of(g);
   size_t b = 3 * al256(z.subseq_f32) + al256(z.drow);   // dqs, dks, dvs, drow
   if (g.io == LH_BF16) b += 2 * al256(rows_bf16(g));     // dos split
   else b += al256(z.subseq_f32);                          // float32 dos
+  if (g.mode == LH_SCATTER_SPAN) b += al256(owner_bytes(g));
   return b;
 }
 
@@ -147,8 +154,9 @@ lh_status lh_get_sizes(const lh_dims *dims, lh_sizes *out) {
   out->token_out_bytes = bh * g.N * g.d * el_size(g.out);
   out->ws_attn_fwd = ws_attn_fwd(g);
   out->ws_attn_bwd = ws_attn_bwd(g);
-  out->ws_layer_fwd = 0;
+  out->ws_layer_fwd = ws_layer_fwd(g);
   out->ws_layer_bwd = ws_layer_bwd(g);
+  out->owner_bytes = owner_bytes(g);
   return LH_OK;
 }
 
@@ -363,6 +371,35 @@ lh_status lh_scatter_bwd(const lh_dims *dims, const void *dout, const int32_t *s
                             nullptr, (hipStream_t)stream);
 }
 
+lh_status lh_span_owner(const lh_dims *dims, const int32_t *row_of, int32_t *owner,
+                        lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(row_of && owner);
+  LH_REQ(aligned4(row_of) && aligned4(owner));
+  return launch_owner(g, row_of, owner, (hipStream_t)stream);
+}
+
+lh_status lh_scatter_span(const lh_dims *dims, const float *os, const int32_t *owner, void *o,
+                          lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(os && owner && o);
+  LH_REQ(aligned16(os) && aligned4(owner) && aligned16(o));
+  return launch_scatter_span(g, os, owner, o, (hipStream_t)stream);
+}
+
+lh_status lh_scatter_span_bwd(const lh_dims *dims, const void *dout, const int32_t *sel_idx,
+                              const uint8_t *sel_flags, const int32_t *owner, float *dos,
+                              lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_REQ(dout && sel_idx && sel_flags && owner && dos);
+  LH_REQ(aligned16(dout) && aligned4(sel_idx) && aligned4(owner) && aligned16(dos));
+  return launch_scatter_span_bwd(g, dout, sel_idx, sel_flags, owner, dos, nullptr, nullptr,
+                                 nullptr, nullptr, (hipStream_t)stream);
+}
+
 lh_status lh_gather_bwd(const lh_dims *dims, const float *dqs, const float *dks,
                         const float *dvs, const int32_t *row_of, void *dq, void *dk, void *dv,
                         lh_stream stream) {
@@ -392,13 +429,13 @@ static lh_status check_saved(const Geo &g, const lh_saved *s) {
 lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const void *v,
                        void *o, const lh_saved *s, void *ws, size_t ws_bytes,
                        lh_stream stream) {
-  (void)ws;
-  (void)ws_bytes;
   Geo g;
   LH_TRY(make_geo(dims, &g));
   LH_REQ(q && k && v && o);
   LH_REQ(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o));
   LH_TRY(check_saved(g, s));
+  const size_t need = ws_layer_fwd(g);
+  if (need && (ws_bytes < need || !ws || !aligned16(ws))) return LH_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   LH_TRY(launch_pyramid_score(g, q, k, v, s->pq, s->pk, s->pv, s->sq, s->sk, st));
   LH_TRY(launch_select(g, s->sq, s->sk, s->sel_idx, s->sel_anchor, s->sel_flags, s->row_of, st));
@@ -412,6 +449,11 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
   else
     LH_TRY(launch_attn_fwd_f32(g, (const float *)s->qs, (const float *)s->ks,
                                (const float *)s->vs, s->sel_flags, (float *)s->os, s->lse, st));
+  if (g.mode == LH_SCATTER_SPAN) {
+    int32_t *owner = (int32_t *)ws;
+    LH_TRY(launch_owner(g, s->row_of, owner, st));
+    return launch_scatter_span(g, (const float *)s->os, owner, o, st);
+  }
   return launch_scatter(g, (const float *)s->os, s->sel_anchor, s->sel_flags, o, st);
 }
 
@@ -431,20 +473,29 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
   float *dks = (float *)c.take(z.subseq_f32);
   float *dvs = (float *)c.take(z.subseq_f32);
   float *drow = (float *)c.take(z.drow);
+  int32_t *owner = g.mode == LH_SCATTER_SPAN ? (int32_t *)c.take(owner_bytes(g)) : nullptr;
+  // scatter adjoint in the layer's mode (dos float32 and/or its bf16 split)
+  auto scatter_adj = [&](float *dos, bf16_t *hi, bf16_t *lo) -> lh_status {
+    if (g.mode == LH_SCATTER_SPAN) {
+      LH_TRY(launch_owner(g, s->row_of, owner, st));
+      return launch_scatter_span_bwd(g, dout, s->sel_idx, s->sel_flags, owner, dos, hi, lo,
+                                     (const float *)s->os, drow, st);
+    }
+    return launch_scatter_bwd(g, dout, s->sel_anchor, s->sel_flags, dos, hi, lo,
+                              (const float *)s->os, drow, st);
+  };
   if (g.io == LH_BF16) {
     bf16_t *dhi = (bf16_t *)c.take(rows_bf16(g));
     bf16_t *dlo = (bf16_t *)c.take(rows_bf16(g));
     if (!c.ok()) return LH_ERR_WORKSPACE;
-    LH_TRY(launch_scatter_bwd(g, dout, s->sel_anchor, s->sel_flags, nullptr, dhi, dlo,
-                              (const float *)s->os, drow, st));
+    LH_TRY(scatter_adj(nullptr, dhi, dlo));
     LH_TRY(launch_attn_bwd_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
                                 (const bf16_t *)s->vs, dhi, dlo, s->lse, drow, s->sel_flags, dqs,
                                 dks, dvs, st));
   } else {
     float *dos = (float *)c.take(z.subseq_f32);
     if (!c.ok()) return LH_ERR_WORKSPACE;
-    LH_TRY(launch_scatter_bwd(g, dout, s->sel_anchor, s->sel_flags, dos, nullptr, nullptr, (const float *)s->os,
-                              drow, st));
+    LH_TRY(scatter_adj(dos, nullptr, nullptr));
     LH_TRY(launch_attn_bwd_f32(g, (const float *)s->qs, (const float *)s->ks,
                                (const float *)s->vs, (const float *)s->os, s->lse, s->sel_flags,
                                dos, drow, dqs, dks, dvs, st));

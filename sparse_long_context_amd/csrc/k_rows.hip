@@ -332,6 +332,192 @@ lh_status launch_scatter_bwd(const Geo &g, const void *dout, const int32_t *sel_
   return hip_status();
 }
 
+// ---------------------------------------------------------------- span broadcast
+// The other reading of the scatter-back: every token takes the output of the
+// finest selected entry whose span holds it (its owner); the stratum root is
+// always selected, so every token has one, and redundant rows own nothing.
+//
+// owner_kernel: owner[t] = row_of(l, t / p^l) for the smallest l at which it
+// is selected; one thread per token, levels walked finest first.
+struct OwnerArgs {
+  const int32_t *row_of;
+  int32_t *owner;
+  int64_t N, E, S;
+  int32_t L, lgp;   // lgp = log2(p) when p is a power of two, else -1
+  int64_t loff[kMaxLevels], pw[kMaxLevels];
+};
+
+__global__ __launch_bounds__(256) void owner_kernel(OwnerArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  if (t >= a.N) return;
+  const int32_t *ro = a.row_of + bh * a.E;
+  int32_t own = -1;
+  for (int l = 0; l < a.L && own < 0; ++l) {
+    const int64_t i = a.lgp >= 0 ? (t >> (a.lgp * l)) : t / a.pw[l];
+    const int32_t r = ro[a.loff[l] + i];
+    if (r >= 0 && r < a.S) own = r;
+  }
+  a.owner[bh * a.N + t] = own;
+}
+
+lh_status launch_owner(const Geo &g, const int32_t *row_of, int32_t *owner, hipStream_t st) {
+  OwnerArgs a;
+  a.row_of = row_of; a.owner = owner; a.N = g.N; a.E = g.E; a.S = g.S; a.L = g.L;
+  a.lgp = -1;
+  for (int k = 0; k < 31; ++k)
+    if ((1 << k) == g.p) a.lgp = k;
+  for (int l = 0; l < kMaxLevels; ++l) {
+    a.loff[l] = g.loff[l];
+    a.pw[l] = l < g.L ? g.pw[l] : 1;
+  }
+  hipLaunchKernelGGL(owner_kernel, dim3(cdiv(g.N, 256), (unsigned)g.BH()), dim3(256), 0, st, a);
+  return hip_status();
+}
+
+// scatter_span_kernel: O[t] = OS[owner[t]], CPR lanes per token row, eight
+// rows in flight per lane.
+template <typename T, int CPR>
+__global__ __launch_bounds__(256) void scatter_span_kernel(const float *os, const int32_t *owner,
+                                                           void *o_, int64_t N, int64_t S,
+                                                           int32_t d) {
+  constexpr int TW = 256 / CPR;   // token lanes
+  constexpr int NF = 8;
+  const int64_t bh = blockIdx.y;
+  const int c = threadIdx.x % CPR;
+  const int64_t t0 = (int64_t)blockIdx.x * (TW * NF) + threadIdx.x / CPR;
+  const float *src = os + bh * S * d + c * 8;
+  T *o = (T *)o_ + bh * N * d + c * 8;
+  const int32_t *own = owner + bh * N;
+  float x[NF][8];
+#pragma unroll
+  for (int k = 0; k < NF; ++k) {
+    const int64_t t = t0 + k * TW;
+    const int32_t r = t < N ? own[t] : -1;
+    if (r >= 0 && r < S) {
+      load8(src + (int64_t)r * d, x[k]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[k][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NF; ++k)
+    if (t0 + k * TW < N) store8(o + (t0 + k * TW) * d, x[k]);
+}
+
+lh_status launch_scatter_span(const Geo &g, const float *os, const int32_t *owner, void *o,
+                              hipStream_t st) {
+  const int cpr = g.d / 8;
+  dim3 grid(cdiv(g.N, (256 / cpr) * 8), (unsigned)g.BH());
+  if (g.out == LH_BF16) {
+    if (g.d == 128) hipLaunchKernelGGL((scatter_span_kernel<bf16_t, 16>), grid, dim3(256), 0, st, os, owner, o, g.N, g.S, g.d);
+    else hipLaunchKernelGGL((scatter_span_kernel<bf16_t, 8>), grid, dim3(256), 0, st, os, owner, o, g.N, g.S, g.d);
+  } else {
+    if (g.d == 128) hipLaunchKernelGGL((scatter_span_kernel<float, 16>), grid, dim3(256), 0, st, os, owner, o, g.N, g.S, g.d);
+    else hipLaunchKernelGGL((scatter_span_kernel<float, 8>), grid, dim3(256), 0, st, os, owner, o, g.N, g.S, g.d);
+  }
+  return hip_status();
+}
+
+// scatter_span_bwd_kernel: dOS[j] = sum of dO[t] over the tokens t of row j's
+// span that it owns.  One wavefront per row; the span's tokens are taken by
+// 64/CPR token lanes in increasing order, NF rows in flight per lane, and the
+// lanes folded in a fixed order.  Writes the same outputs as the hold adjoint.
+struct SpanBwdArgs {
+  const void *dout;
+  const int32_t *sel_idx, *owner;
+  const uint8_t *flags;
+  float *dos;
+  bf16_t *dos_hi, *dos_lo;
+  const float *os;
+  float *drow;
+  int64_t N, S, E;
+  int32_t d, L;
+  int64_t loff[kMaxLevels], pw[kMaxLevels];
+};
+
+template <typename T, int CPR>
+__global__ __launch_bounds__(256) void scatter_span_bwd_kernel(SpanBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t bh = blockIdx.y;
+  if (j >= a.S) return;
+  const int d = a.d;
+  const int c = lane % CPR, u = lane / CPR;
+  constexpr int TL = 64 / CPR;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (!(a.flags[bh * a.S + j] & LH_ROW_REDUNDANT)) {
+    const int64_t f = a.sel_idx[bh * a.S + j];
+    int l = 0;
+    while (l + 1 < a.L && f >= a.loff[l + 1]) ++l;
+    const int64_t span = a.pw[l];
+    const int64_t t0 = min(max((int64_t)0, (f - a.loff[l]) * span), a.N);
+    const int64_t t1 = min(t0 + span, a.N);
+    const T *dO = (const T *)a.dout + bh * a.N * d + c * 8;
+    const int32_t *own = a.owner + bh * a.N;
+    constexpr int NF = sizeof(T) == 2 ? 16 : 8;
+    for (int64_t t = t0 + u; t < t1; t += NF * TL) {
+      Raw8<T> x[NF];
+      bool mine[NF];
+#pragma unroll
+      for (int k = 0; k < NF; ++k) {
+        const int64_t tk = t + k * TL;
+        mine[k] = tk < t1 && own[tk] == (int32_t)j;
+        if (mine[k]) x[k].load(dO + tk * d);
+      }
+#pragma unroll
+      for (int k = 0; k < NF; ++k)
+        if (mine[k]) x[k].add_to(acc);
+    }
+#pragma unroll
+    for (int off = CPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], off);
+  }
+  const int64_t row = (bh * a.S + j) * d + c * 8;
+  if (u == 0) {
+    if (a.dos) store8(a.dos + row, acc);
+    if (a.dos_hi) store8_split(a.dos_hi + row, a.dos_lo + row, acc);
+  }
+  if (a.drow) {
+    float o[8];
+    load8(a.os + row, o);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += acc[i] * o[i];
+#pragma unroll
+    for (int off = 1; off < CPR; off <<= 1) s += __shfl_xor(s, off);
+    if (lane == 0) a.drow[bh * a.S + j] = s;
+  }
+}
+
+lh_status launch_scatter_span_bwd(const Geo &g, const void *dout, const int32_t *sel_idx,
+                                  const uint8_t *sel_flags, const int32_t *owner, float *dos,
+                                  bf16_t *dos_hi, bf16_t *dos_lo, const float *os, float *drow,
+                                  hipStream_t st) {
+  SpanBwdArgs a;
+  a.dout = dout; a.sel_idx = sel_idx; a.owner = owner; a.flags = sel_flags; a.dos = dos;
+  a.dos_hi = dos_lo ? dos_hi : nullptr; a.dos_lo = dos_lo;
+  a.os = os; a.drow = os ? drow : nullptr; a.N = g.N; a.S = g.S; a.E = g.E; a.d = g.d;
+  a.L = g.L;
+  for (int l = 0; l < kMaxLevels; ++l) {
+    a.loff[l] = l < g.L ? g.loff[l] : g.E;
+    a.pw[l] = l < g.L ? g.pw[l] : 1;
+  }
+  dim3 grid(cdiv(g.S, 4), (unsigned)g.BH());
+  if (g.out == LH_BF16) {
+    if (g.d == 128) hipLaunchKernelGGL((scatter_span_bwd_kernel<bf16_t, 16>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((scatter_span_bwd_kernel<bf16_t, 8>), grid, dim3(256), 0, st, a);
+  } else {
+    if (g.d == 128) hipLaunchKernelGGL((scatter_span_bwd_kernel<float, 16>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((scatter_span_bwd_kernel<float, 8>), grid, dim3(256), 0, st, a);
+  }
+  return hip_status();
+}
+
 // ---------------------------------------------------------------- dOS prologue
 // float32 dOS -> optional bf16 split (hi, lo) and drow = <dOS_j, OS_j>; one
 // wavefront per row.

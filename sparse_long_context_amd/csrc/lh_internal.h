@@ -19,6 +19,7 @@ struct Geo {
   int64_t B, N, K, S, E, n_c, T, k_s, Bc, Sp;
   int32_t H, d, p, L;
   int32_t io, out;
+  int32_t mode;                  // LH_SCATTER_HOLD or LH_SCATTER_SPAN
   float scale;                   // softmax scale (1/sqrt(d) when dims say 0)
   int64_t lsize[kMaxLevels];     // N / p^l
   int64_t loff[kMaxLevels];      // flat offset of level l
@@ -124,6 +125,15 @@ lh_status launch_scatter(const Geo &g, const float *os, const int32_t *sel_ancho
 lh_status launch_scatter_bwd(const Geo &g, const void *dout, const int32_t *sel_anchor,
                              const uint8_t *sel_flags, float *dos, bf16_t *dos_hi,
                              bf16_t *dos_lo, const float *os, float *drow, hipStream_t st);
+// span broadcast: owner[BH, N] int32 (finest selected entry per token), the
+// copy O[t] = OS[owner[t]], and its adjoint (outputs as launch_scatter_bwd)
+lh_status launch_owner(const Geo &g, const int32_t *row_of, int32_t *owner, hipStream_t st);
+lh_status launch_scatter_span(const Geo &g, const float *os, const int32_t *owner, void *o,
+                              hipStream_t st);
+lh_status launch_scatter_span_bwd(const Geo &g, const void *dout, const int32_t *sel_idx,
+                                  const uint8_t *sel_flags, const int32_t *owner, float *dos,
+                                  bf16_t *dos_hi, bf16_t *dos_lo, const float *os, float *drow,
+                                  hipStream_t st);
 lh_status launch_unpool(const Geo &g, const float *const dxs[3], const int32_t *row_of,
                         void *const dx[3], hipStream_t st);
 

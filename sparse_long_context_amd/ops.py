@@ -34,14 +34,18 @@ def _need(t, shape, dtype, name):
         raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
 
 
-def make_dims(q: torch.Tensor, p: int, L_: int, S: int, out_dtype=None, scale: float = 0.0):
+SCATTER_MODES = {"hold": L.LH_SCATTER_HOLD, "span": L.LH_SCATTER_SPAN}
+
+
+def make_dims(q: torch.Tensor, p: int, L_: int, S: int, out_dtype=None, scale: float = 0.0,
+              scatter_mode: str = "hold"):
     """Dims of a call on q [B, H, N, d]; K is S minus the n_c kept roots."""
     B, H, N, d = q.shape
     Bc = p ** (L_ - 1)
     n_c = N // Bc if Bc <= N else 0
     io = LHDT[q.dtype]
     out = io if out_dtype is None else LHDT[out_dtype]
-    return L.make_dims(B, N, H, d, p, L_, S - n_c, S, io, out, scale)
+    return L.make_dims(B, N, H, d, p, L_, S - n_c, S, io, out, scale, SCATTER_MODES[scatter_mode])
 
 
 class Ctx:
@@ -238,6 +242,27 @@ def _saved_struct(s):
     return L.Saved(*[None if s[f] is None else s[f].data_ptr() for f in SAVED_FIELDS])
 
 
+def span_owner(c: Ctx, row_of):
+    owner = c.empty(*_bh(c), c.N, dtype=torch.int32, device=row_of.device)
+    c.call("lh_span_owner", _ptr(row_of), _ptr(owner), _stream())
+    return owner
+
+
+def scatter_span(c: Ctx, os_, owner):
+    _need(os_, _bh(c) + (c.S, c.d), torch.float32, "os")
+    o = c.empty(*_bh(c), c.N, c.d, dtype=c.out, device=os_.device)
+    c.call("lh_scatter_span", _ptr(os_), _ptr(owner), _ptr(o), _stream())
+    return o
+
+
+def scatter_span_bwd(c: Ctx, dout, sel_idx, sel_flags, owner):
+    _need(dout, _bh(c) + (c.N, c.d), c.out, "dout")
+    dos = c.empty(*_bh(c), c.S, c.d, dtype=torch.float32, device=dout.device)
+    c.call("lh_scatter_span_bwd", _ptr(dout), _ptr(sel_idx), _ptr(sel_flags), _ptr(owner),
+           _ptr(dos), _stream())
+    return dos
+
+
 def layer_fwd(c: Ctx, q, k, v, saved=None, o=None):
     dev = q.device
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -245,8 +270,10 @@ def layer_fwd(c: Ctx, q, k, v, saved=None, o=None):
     saved = alloc_saved(c, dev) if saved is None else saved
     o = c.empty(*_bh(c), c.N, c.d, dtype=c.out, device=dev) if o is None else o
     st = _saved_struct(saved)
-    c.call("lh_layer_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), C.byref(st), None,
-           C.c_size_t(0), _stream())
+    nws = c.z.ws_layer_fwd
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    c.call("lh_layer_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), C.byref(st),
+           None if ws is None else _ptr(ws), C.c_size_t(nws), _stream())
     return o, saved
 
 

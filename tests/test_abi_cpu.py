@@ -69,11 +69,26 @@ def test_validate(lib, kw, code):
     assert lib.lh_validate(C.byref(dims(**kw))) == code
 
 
-def test_validate_null_and_reserved(lib):
+def test_validate_null_and_scatter_mode(lib):
     assert lib.lh_validate(None) == L.LH_ERR_INVALID_ARG
     d = dims()
-    d.reserved = 1
-    assert lib.lh_validate(C.byref(d)) == L.LH_ERR_INVALID_ARG
+    for mode, code in ((L.LH_SCATTER_HOLD, L.LH_OK), (L.LH_SCATTER_SPAN, L.LH_OK), (2, L.LH_ERR_INVALID_ARG),
+                       (-1, L.LH_ERR_INVALID_ARG)):
+        d.scatter_mode = mode
+        assert lib.lh_validate(C.byref(d)) == code, mode
+
+
+def test_span_mode_workspace_holds_the_owner_map(lib):
+    d = dims(N=131072, H=8, d=128, p=4, L=6, K=8064, S=8192, io_dtype=L.LH_BF16,
+             out_dtype=L.LH_BF16)
+    hold, span = L.Sizes(), L.Sizes()
+    assert lib.lh_get_sizes(C.byref(d), C.byref(hold)) == L.LH_OK
+    d.scatter_mode = L.LH_SCATTER_SPAN
+    assert lib.lh_get_sizes(C.byref(d), C.byref(span)) == L.LH_OK
+    owner = 8 * 131072 * 4
+    assert hold.owner_bytes == span.owner_bytes == owner
+    assert hold.ws_layer_fwd == 0 and span.ws_layer_fwd >= owner
+    assert span.ws_layer_bwd >= hold.ws_layer_bwd + owner
 
 
 def test_sizes_c4_shape(lib):
@@ -119,6 +134,18 @@ def test_stage_calls_reject_bad_args_without_launch(lib):
     s = L.Saved(*([0x10000] * 17))
     assert lib.lh_layer_bwd(C.byref(d2), C.byref(s), p, p, p, p, None, 0, None) == \
         L.LH_ERR_WORKSPACE
+    # span mode: the forward needs a workspace for the owner map
+    d3 = dims(io_dtype=L.LH_BF16, out_dtype=L.LH_BF16)
+    d3.scatter_mode = L.LH_SCATTER_SPAN
+    assert lib.lh_layer_fwd(C.byref(d3), p, p, p, p, C.byref(s), None, 0, None) == \
+        L.LH_ERR_WORKSPACE
+    # span-mode stage calls
+    assert lib.lh_span_owner(C.byref(d), None, p, None) == L.LH_ERR_INVALID_ARG
+    assert lib.lh_span_owner(C.byref(d), p, bad, None) == L.LH_ERR_INVALID_ARG
+    assert lib.lh_scatter_span(C.byref(d), p, p, None, None) == L.LH_ERR_INVALID_ARG
+    assert lib.lh_scatter_span(C.byref(d), bad, p, p, None) == L.LH_ERR_INVALID_ARG
+    assert lib.lh_scatter_span_bwd(C.byref(d), p, p, p, None, p, None) == L.LH_ERR_INVALID_ARG
+    assert lib.lh_scatter_span_bwd(C.byref(dd), p, p, p, p, p, None) == L.LH_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

@@ -19,11 +19,12 @@ if torch.cuda.is_available():
     from sparse_long_context_amd import ops
 
 
-def _ctx(case, q):
+def _ctx(case, q, scatter_mode="hold"):
     out = torch.float32 if case.out == "f32" else torch.bfloat16
     if case.dtype == "f32":
         out = torch.float32
-    return ops.Ctx(ops.make_dims(q, case.p, case.L, case.S, out_dtype=out))
+    return ops.Ctx(ops.make_dims(q, case.p, case.L, case.S, out_dtype=out,
+                                 scatter_mode=scatter_mode))
 
 
 @pytest.fixture(scope="module")
@@ -217,6 +218,60 @@ def test_layer_matches_stages_and_is_deterministic(case, dev):
     assert torch.equal(o1, r["o"])
     for a, n in zip(g1, ("dq", "dk", "dv")):
         assert torch.equal(a, r[n]), n
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_span_scatter_and_adjoint(case, dev):
+    """Span broadcast: the owner map bit-exact, the scatter a pure copy, its
+    adjoint within float32 summation error of the oracle."""
+    r = stages(case, dev)
+    c = r["c"]
+    g = geometry(case)
+    owner = ops.span_owner(c, r["row_of"])
+    o = ops.scatter_span(c, r["os"], owner)
+    dos = ops.scatter_span_bwd(c, r["dO"], r["sel_idx"], r["flags"], owner)
+    torch.cuda.synchronize()
+    for h in range(case.H):
+        sel = selection_from_gpu(g, *(r[n][0, h].cpu().numpy() for n in ("sel_idx", "anchor", "flags", "row_of")))
+        own = orc.span_owner(sel, g)
+        assert np.array_equal(owner[0, h].cpu().numpy(), own), f"owner head {h}"
+        want = r["os"][0, h][torch.from_numpy(own).to(dev)].to(o.dtype)
+        assert torch.equal(o[0, h], want), "span scatter is a pure copy"
+        dOS = orc.scatter_span_adjoint(f64(r["dO"][0, h]), sel, g)
+        got = f64(dos[0, h])
+        assert np.all(np.abs(got - dOS) <= 1e-5 * (1 + np.abs(dOS))), float(np.max(np.abs(got - dOS)))
+
+
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_layer_span_mode_vs_oracle(case, dev):
+    """lh_layer_fwd/bwd in span-broadcast mode against the oracle; the layer
+    equals its stages bitwise and two runs are identical."""
+    Q, K, V, dO = (t.to(dev) for t in inputs(case))
+    c = _ctx(case, Q, scatter_mode="span")
+    o, saved = ops.layer_fwd(c, Q, K, V)
+    dOc = dO.to(c.out)
+    dq, dk, dv = ops.layer_bwd(c, saved, dOc)
+    o2, saved2 = ops.layer_fwd(c, Q, K, V)
+    g2 = ops.layer_bwd(c, saved2, dOc)
+    owner = ops.span_owner(c, saved["row_of"])
+    dos = ops.scatter_span_bwd(c, dOc, saved["sel_idx"], saved["sel_flags"], owner)
+    sq = ops.subseq_attn_bwd(c, saved["qs"], saved["ks"], saved["vs"], saved["os"], saved["lse"],
+                             saved["sel_flags"], dos)
+    stage_grads = ops.gather_bwd(c, *sq, saved["row_of"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and all(torch.equal(a, b) for a, b in zip((dq, dk, dv), g2))
+    assert torch.equal(o, ops.scatter_span(c, saved["os"], owner))
+    for a, b, n in zip((dq, dk, dv), stage_grads, ("dq", "dk", "dv")):
+        assert torch.equal(a, b), n
+    g = geometry(case)
+    for h in range(case.H):
+        fw = orc.head_forward(f64(Q[0, h]), f64(K[0, h]), f64(V[0, h]), g, store=store_of(case),
+                              scatter_mode="span")
+        assert np.array_equal(saved["sel_idx"][0, h].cpu().numpy(), fw.sel.sel_idx)
+        _close(f64(o[0, h]), fw.O, tol_for(case, fw.O, case.out), f"{case.name} h{h} span O")
+        gq, gk, gv = orc.head_backward(fw, f64(dOc[0, h]))[:3]
+        for got, want, n in ((dq, gq, "dQ"), (dk, gk, "dK"), (dv, gv, "dV")):
+            _close(f64(got[0, h]), want, tol_for(case, want, case.out), f"{case.name} h{h} span {n}")
 
 
 def test_full_selection_is_dense_sdpa(dev):
