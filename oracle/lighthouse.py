@@ -163,20 +163,31 @@ def pyramid(X, g: Geometry, store: str | None = None):
     R-2: the pooled levels are tensors of the layer's I/O dtype.  With
     store='bf16' (or 'f32') each coarse level is rounded once, from the
     exact mean, to bfloat16 (float32); the rounding does not feed the next
-    level's mean.
+    level's mean.  The exact mean of a level-l entry is the mean of the p^l
+    tokens it covers (the recursion unrolled); it is formed here as that
+    block's float64 sum divided by p^l.  For bf16 or float32 inputs the
+    sum is exact (unless one block's magnitudes span some thirty binades or
+    more) and the division rounds at most once, and not at all when the
+    mean is representable, as every bf16 rounding tie is.  The recursive
+    float64 means above carry a rounding per level when p is not a power
+    of two, which can move a tie by one float64 step and flip its rounding.
     """
     X = np.asarray(X, dtype=np.float64)
     levels = [X]
     for _ in range(1, g.L):
         prev = levels[-1]
         levels.append(prev.reshape(prev.shape[0] // g.p, g.p, -1).mean(axis=1))
-    if store == "bf16":
-        levels = [levels[0]] + [round_bf16(Y) for Y in levels[1:]]
-    elif store == "f32":
-        levels = [levels[0]] + [Y.astype(np.float32).astype(np.float64) for Y in levels[1:]]
-    elif store is not None:
+    if store is None:
+        return levels
+    if store not in ("bf16", "f32"):
         raise ValueError(store)
-    return levels
+    out = [X]
+    for l in range(1, g.L):
+        w = g.p ** l
+        exact = X.reshape(X.shape[0] // w, w, -1).sum(axis=1) / w
+        out.append(round_bf16(exact) if store == "bf16"
+                   else exact.astype(np.float32).astype(np.float64))
+    return out
 
 
 def flat_rows(levels):

@@ -8,6 +8,8 @@ tests/golden/.  CPU only.
 import json
 import os
 
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -73,20 +75,49 @@ def test_pyramid_is_brute_force_mean(N, p, L):
         np.testing.assert_allclose(lv[l], brute, rtol=0, atol=1e-14)
 
 
-def test_pyramid_bf16_store_rounds_exact_mean_once():
-    g = orc.Geometry(256, 4, 4, 0)
-    X = orc.round_bf16(rnd((256, 8), 3))
-    exact = orc.pyramid(X, g)
-    st = orc.pyramid(X, g, store="bf16")
+def _round_exact(q, bits):
+    """Round the rational q to the nearest binary float with `bits`
+    significant bits, ties to even, in exact rational arithmetic (normal
+    range only)."""
+    if q == 0:
+        return q
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    unit = Fraction(2) ** (e - bits + 1)
+    n, rem = divmod(a, unit)
+    if rem > unit / 2 or (rem == unit / 2 and n % 2 == 1):
+        n += 1
+    return (n * unit) if q > 0 else -(n * unit)
+
+
+@pytest.mark.parametrize("store,bits,N,p,L", [("bf16", 8, 486, 3, 4), ("bf16", 8, 256, 4, 4),
+                                             ("f32", 24, 243, 3, 4), ("bf16", 8, 250, 5, 3)])
+def test_pyramid_store_rounds_exact_mean_once(store, bits, N, p, L):
+    # R-2: a stored coarse entry is the exact mean of the p^l tokens it
+    # covers, rounded once (ties to even).  Means of bf16 values land
+    # exactly on a bf16 rounding tie often enough (dozens of times here)
+    # to catch a chain of rounded float64 means, which moves some ties when
+    # p is not a power of two.  Exact rational arithmetic throughout.
+    g = orc.Geometry(N, p, L, 0)
+    X = torch.from_numpy(rnd((N, 8), 41))
+    X = (X.to(torch.bfloat16) if store == "bf16" else X.float()).double().numpy()
+    st = orc.pyramid(X, g, store=store)
     assert np.array_equal(st[0], X)
-    for l in range(1, 4):
-        w = 4 ** l
-        brute = np.array([X[i * w:(i + 1) * w].mean(axis=0) for i in range(256 // w)])
-        t = torch.from_numpy(brute.astype(np.float32)).to(torch.bfloat16).double().numpy()
-        # brute mean is exact in float32 here? not always: compare to within
-        # one bf16 step and require equality with rounding of the exact mean
-        assert np.array_equal(st[l], orc.round_bf16(exact[l]))
-        assert np.max(np.abs(st[l] - t)) <= np.max(np.abs(t)) * 2.0 ** -7
+    ties = 0
+    for l in range(1, L):
+        w = p ** l
+        for i in range(N // w):
+            for j in range(X.shape[1]):
+                q = sum(Fraction(float(v)) for v in X[i * w:(i + 1) * w, j]) / w
+                want = _round_exact(q, bits)
+                assert Fraction(float(st[l][i, j])) == want, (l, i, j)
+                ties += _round_exact(q, bits + 1) == q and _round_exact(q, bits) != q
+    if store == "bf16":
+        assert ties >= 10      # the input really exercises the tie rule
 
 
 # ---------------------------------------------------------------- O2 scores
