@@ -17,9 +17,14 @@
 // LDS, where levels g+1..L-1 of each stratum are formed.  Every input byte is
 // read once and every output byte written once; the kernel is HBM-bound.
 //
-// Rounding: sums are float32; each pyramid entry is rounded once from its
-// float32 sum (sum / p^l) to the I/O type.  Squares of a row are summed in
-// float64 and the square root is rounded once to float32.
+// Rounding: sums are float64, which holds the sum of a cell's bf16 or
+// float32 inputs exactly unless their magnitudes span tens of binades; the
+// mean sum / p^l is formed in float64 (exact whenever the mean is
+// representable, as every rounding tie is) and then rounded once to the I/O
+// type.  A float32 sum would round twice (the sum, then the mean) and, for p
+// not a power of two, move some means across a bf16 rounding boundary.
+// Squares of a row are summed in float64 and the square root is rounded once
+// to float32.
 #include "lh_internal.h"
 
 namespace lh {
@@ -35,8 +40,40 @@ struct PyrArgs {
   int32_t d, p, L, g, R, spw;
   int64_t lsize[kMaxLevels], loff[kMaxLevels], pw[kMaxLevels + 1];
   int64_t per[kMaxLevels];   // entries of level l per stratum (Bc / p^l)
-  float rp[kMaxLevels];      // 1 / p^l
+  double rp[kMaxLevels];     // 1 / p^l
+  double pwd[kMaxLevels];    // p^l
+  int32_t pow2;              // p is a power of two: 1 / p^l is exact
 };
+
+// float64 -> float32 rounding to odd: truncate toward zero and set the last
+// bit when anything was dropped.  Rounding that result to a format with at
+// least two fewer significant bits (bf16 keeps 8 of float32's 24) gives the
+// same value as rounding the float64 directly, so the float32 -> bf16
+// convert of the store is the only rounding that counts.
+__device__ __forceinline__ float f64_to_f32_odd(double x) {
+  const float f = (float)x;
+  uint32_t b = __float_as_uint(f);
+  const double back = (double)f;
+  const bool inexact = back != x;
+  b -= (inexact && fabs(back) > fabs(x)) ? 1u : 0u;   // rounded away: step back
+  b |= inexact ? 1u : 0u;
+  return __uint_as_float(b);
+}
+
+// the mean sum / p^l of a level-l entry, as the float32 that the store
+// rounds to T: float32 I/O rounds the float64 mean to nearest once; bf16 I/O
+// rounds it to odd here and to nearest-even in the store.  The mean is a
+// multiply by the exact reciprocal when p is a power of two, else a
+// correctly rounded division.
+template <typename T>
+__device__ __forceinline__ float level_mean(const PyrArgs &a, double sum, int l) {
+  const double m = a.pow2 ? sum * a.rp[l] : sum / a.pwd[l];
+  if constexpr (sizeof(T) == 2) {
+    return f64_to_f32_odd(m);
+  } else {
+    return (float)m;
+  }
+}
 
 // a float64 moved across lanes by one DPP pattern (both halves)
 template <int CTRL>
@@ -80,9 +117,37 @@ __device__ __forceinline__ float group_bcast(float v, int u) {
   return __int_as_float(r);
 }
 
+// U token rows of 8 columns held in their I/O encoding until used: bf16
+// rows stay packed (4 registers a row instead of 8), float rows as they are
+template <typename T, int U> struct RowBuf;
+template <int U> struct RowBuf<bf16_t, U> {
+  uint32_t w[U][4];
+  __device__ __forceinline__ void load(int u, const bf16_t *p) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(p);
+    w[u][0] = a.x; w[u][1] = a.y; w[u][2] = a.z; w[u][3] = a.w;
+  }
+  __device__ __forceinline__ void zero(int u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[u][i] = 0u;
+  }
+  __device__ __forceinline__ float get(int u, int i) const {
+    const uint32_t v = w[u][i >> 1];
+    return __uint_as_float((i & 1) ? (v & 0xffff0000u) : (v << 16));
+  }
+};
+template <int U> struct RowBuf<float, U> {
+  float x[U][8];
+  __device__ __forceinline__ void load(int u, const float *p) { load8(p, x[u]); }
+  __device__ __forceinline__ void zero(int u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[u][i] = 0.f;
+  }
+  __device__ __forceinline__ float get(int u, int i) const { return x[u][i]; }
+};
+
 template <typename T, int CPR, int G>
 __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
-  extern __shared__ float lds[];                 // [spw*R][d] sums, then [spw*R] maxima
+  extern __shared__ double lds[];                // [spw*R][d] sums, then [spw*R] maxima
   constexpr int U = 8;                           // token rows in flight per thread
   const int z = blockIdx.z;
   const T *X = (const T *)a.in[z];
@@ -102,13 +167,13 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
   const int Gt = (int)a.pw[G];             // tokens of the subtree
   const int64_t base = m * a.Bc + (int64_t)r * Gt;
   const int rows = a.spw * a.R;
-  float *lsum = lds;                       // [rows][d]
-  float *lmax = lds + (size_t)rows * d;    // [rows]
+  double *lsum = lds;                                  // [rows][d]
+  float *lmax = reinterpret_cast<float *>(lds + (size_t)rows * d);   // [rows]
 
   // running sums / maxima of the levels 1..G entries being completed, the
   // children each has taken so far, and the index (within its level) of the
   // entry it will complete next
-  float acc[G + 1][8];
+  double acc[G + 1][8];
   float smx[G + 1];
   int cnt[G + 1];
   int64_t idx[G + 1];
@@ -118,18 +183,17 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
     cnt[l] = 0;
     idx[l] = m * a.per[l] + (int64_t)r * a.pw[G - l];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[l][i] = 0.f;
+    for (int i = 0; i < 8; ++i) acc[l][i] = 0.0;
   }
 
   for (int t0 = 0; t0 < Gt; t0 += U) {
-    float x[U][8];
+    RowBuf<T, U> x;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t0 + u < Gt) {
-        load8(X + (base + t0 + u) * d + c * 8, x[u]);
+        x.load(u, X + (base + t0 + u) * d + c * 8);
       } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[u][i] = 0.f;
+        x.zero(u);
       }
     }
     // l2 norms of the U rows: float64 sums of squares over the row group;
@@ -137,18 +201,19 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
     // receives all U norms
     float s_all[U];
     if (do_sc) {
-      double ss[U];
+      const int own = c & (U - 1);
+      double mine = 0.0;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         double t = 0.0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) t += (double)x[u][i] * (double)x[u][i];
-        ss[u] = rowsum_f64<CPR>(t);
+        for (int i = 0; i < 8; ++i) {
+          const double v = (double)x.get(u, i);
+          t += v * v;
+        }
+        t = rowsum_f64<CPR>(t);
+        mine = own == u ? t : mine;
       }
-      const int own = c & (U - 1);
-      double mine = ss[0];
-#pragma unroll
-      for (int u = 1; u < U; ++u) mine = own == u ? ss[u] : mine;
       const float s_own = (float)sqrt(mine);
       if (c < U && t0 + c < Gt) Sc[base + t0 + c] = s_own;
 #pragma unroll
@@ -164,11 +229,11 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
       if constexpr (G == 0) {
         // the subtree is a single token: it goes straight to LDS
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lsum[(size_t)rs * d + c * 8 + i] = x[u][i];
+        for (int i = 0; i < 8; ++i) lsum[(size_t)rs * d + c * 8 + i] = x.get(u, i);
         if (c == 0) lmax[rs] = s;
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[1][i] += x[u][i];
+        for (int i = 0; i < 8; ++i) acc[1][i] += (double)x.get(u, i);
         smx[1] = fmaxf(smx[1], s);
 #pragma unroll
         for (int l = 1; l <= G; ++l) {
@@ -177,7 +242,7 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
           if (do_pyr) {
             float mean[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) mean[i] = acc[l][i] * a.rp[l];
+            for (int i = 0; i < 8; ++i) mean[i] = level_mean<T>(a, acc[l][i], l);
             store8(P + (a.loff[l] - a.N + idx[l]) * d + c * 8, mean);
           }
           if (do_sc && c == 0) Sc[a.loff[l] + idx[l]] = smx[l];
@@ -192,7 +257,7 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
             smx[l + 1] = fmaxf(smx[l + 1], smx[l]);
           }
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[l][i] = 0.f;
+          for (int i = 0; i < 8; ++i) acc[l][i] = 0.0;
           smx[l] = 0.f;
         }
       }
@@ -207,11 +272,11 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
     n /= a.p;
     const bool act = rs < a.spw * n;
     const int s2 = act ? rs / n : 0, e = act ? rs % n : 0;
-    float sum[8];
+    double sum[8];
     float mx = 0.f;
     if (act) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sum[i] = 0.f;
+      for (int i = 0; i < 8; ++i) sum[i] = 0.0;
       for (int k = 0; k < a.p; ++k) {
         const int row = s2 * a.R + e * a.p + k;
 #pragma unroll
@@ -230,7 +295,7 @@ __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
       if (do_pyr) {
         float mean[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) mean[i] = sum[i] * a.rp[l];
+        for (int i = 0; i < 8; ++i) mean[i] = level_mean<T>(a, sum[i], l);
         store8(P + (a.loff[l] - a.N + idx) * d + c * 8, mean);
       }
       if (do_sc && c == 0) Sc[a.loff[l] + idx] = mx;
@@ -277,8 +342,10 @@ lh_status launch_pyramid_score(const Geo &g, const void *q, const void *k, const
   for (int l = 0; l <= kMaxLevels; ++l) a.pw[l] = g.pw[l];
   for (int l = 0; l < kMaxLevels; ++l) {
     a.per[l] = l < g.L ? g.Bc / g.pw[l] : 0;
-    a.rp[l] = l < g.L ? (float)(1.0 / (double)g.pw[l]) : 0.f;
+    a.rp[l] = l < g.L ? 1.0 / (double)g.pw[l] : 0.0;
+    a.pwd[l] = l < g.L ? (double)g.pw[l] : 1.0;
   }
+  a.pow2 = (g.p & (g.p - 1)) == 0;
   if (!pyr_plan(g, &a.g, &a.R, &a.spw)) return LH_ERR_UNSUPPORTED;
   int nz = 0;
   for (int z = 0; z < 3; ++z) nz = a.in[z] ? z + 1 : nz;
@@ -286,7 +353,7 @@ lh_status launch_pyramid_score(const Geo &g, const void *q, const void *k, const
   const int cpr = g.d / 8;
   dim3 grid((unsigned)(g.n_c / a.spw), (unsigned)g.BH(), (unsigned)nz);
   dim3 block((unsigned)(a.spw * a.R * cpr));
-  const size_t shm = (size_t)a.spw * a.R * (g.d + 1) * sizeof(float);
+  const size_t shm = (size_t)a.spw * a.R * ((size_t)g.d * sizeof(double) + sizeof(float));
 #define LH_PYR_G(T, C, GG) \
   case GG: hipLaunchKernelGGL((pyr_score_kernel<T, C, GG>), grid, block, shm, st, a); break;
 #define LH_PYR(T, C)                                                                          \

@@ -27,6 +27,7 @@ class Case:
     structure: str = "none"
     out: str = "f32"          # output dtype of the parity run
     seed: int = 1234
+    B: int = 1                # batch; heads of the generator are split into batches
 
     @property
     def n_c(self):
@@ -56,13 +57,25 @@ CASES = [
     Case("bf16-L1-dense", 768, 1, 64, 2, 1, 0),
     # bursts of high-norm tokens, d=128, bf16 outputs
     Case("bf16-bursts-bf16out", 8192, 2, 128, 4, 5, 15, structure="bursts", out="bf16"),
+    # batch 2 (flattened (b, h) indexing), p = 2 with six levels: B_c = 32, S = 384
+    Case("bf16-batch2-p2", 2048, 3, 64, 2, 6, 5, B=2),
+    # p = 3, not a power of two (division instead of shifts): B_c = 27, S = 440
+    Case("bf16-p3", 1080, 2, 64, 3, 4, 10, structure="spikes"),
+    # a single coarsest cell: n_c = 1, S = 101 (less than one tile)
+    Case("bf16-one-stratum", 1024, 2, 128, 4, 6, 100),
 ]
 
 
 def inputs(case: Case):
-    w = synth.Workload(0, case.name, case.N, case.H, case.d, case.p, case.L, case.S, case.dtype,
-                       case.structure)
-    return synth.make_inputs(w, seed=case.seed)
+    """Q, K, V, dO [B, H, N, d]: the generator's B*H heads, split into batches."""
+    w = synth.Workload(0, case.name, case.N, case.B * case.H, case.d, case.p, case.L, case.S,
+                       case.dtype, case.structure)
+    return tuple(t.reshape(case.B, case.H, case.N, case.d)
+                 for t in synth.make_inputs(w, seed=case.seed))
+
+
+def bh_pairs(case: Case):
+    return [(b, h) for b in range(case.B) for h in range(case.H)]
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
