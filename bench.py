@@ -9,9 +9,10 @@ Prints ONE JSON line.  Besides the headline (tokens/s of fwd+bwd), it reports
 per-stage times with algorithmic GB/s or TFLOP/s (stage mode: every stage
 entry point timed alone with HIP events on the stream its kernels run on),
 a roofline object for the dominant kernel, the device's measured HBM-copy
-and MFMA ceilings, dense causal attention over all N tokens (torch's fused
-SDPA) as the comparison point, and the CPU oracle timed on a bounded sample
-of the same workload.
+and MFMA ceilings, dense causal attention over all N tokens as the
+comparison point (torch's fused SDPA, and this library's own MFMA kernels
+run as the one-level layer), and the CPU oracle timed on a bounded sample of
+the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 4]
                        [--no-cpu] [--no-stages] [--no-dense]
@@ -44,7 +45,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
-                    help="skip the dense causal SDPA comparison (about 1 s at the 128K workload)")
+                    help="skip the dense causal attention comparisons, torch SDPA and this "
+                         "library's kernels at L=1 (a few seconds at the 128K workload)")
     ap.add_argument("--stage-reps", type=int, default=10)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known byte "
@@ -183,11 +185,39 @@ def dense_sdpa(torch, Q, K, V, dO, reps=2):
                 torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
             if best is None or ms < best[1]:
-                best = (backend.name, ms)
+                best = (backend.name, ms, backend)
             del q, k, v
         except RuntimeError as ex:
             print(f"[bench] dense SDPA {backend.name} unavailable: {ex}", file=sys.stderr, flush=True)
     return best
+
+
+def dense_own(torch, ops, Q, K, V, dO, reps=2):
+    """Dense causal attention over all N tokens on this library's own MFMA
+    kernels: the layer with one level (L = 1, so S = N and no row is
+    redundant), forward and backward on the same inputs.  Returns the time
+    per step and the output, for a check against torch's SDPA."""
+    dev = Q.device
+    c = ops.Ctx(ops.make_dims(Q, 2, 1, Q.shape[2], out_dtype=dO.dtype))
+    saved = ops.alloc_saved(c, dev)
+    o = torch.empty_like(Q, dtype=dO.dtype)
+    ws = torch.empty(max(1, c.z.ws_layer_bwd), dtype=torch.uint8, device=dev)
+    grads = [torch.empty_like(Q, dtype=dO.dtype) for _ in range(3)]
+
+    def run():
+        ops.layer_fwd(c, Q, K, V, saved=saved, o=o)
+        ops.layer_bwd(c, saved, dO, ws=ws, outs=grads)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    del saved, ws, grads
+    return e0.elapsed_time(e1) / reps, o
 
 
 def main():
@@ -305,7 +335,7 @@ def main():
         for n, e in stages.items():
             print(f"[bench] stage {n:20s} {e}", file=sys.stderr, flush=True)
 
-    dense = None
+    dense = dense_mine = None
     if not args.no_dense and w.dtype == "bf16":
         best = dense_sdpa(torch, Q, K, V, dO)
         if best:
@@ -315,6 +345,21 @@ def main():
                      "what": "dense causal attention over all N tokens, forward+backward, "
                              "torch fused SDPA on the same inputs"}
             print(f"[bench] dense SDPA {dense}", file=sys.stderr, flush=True)
+        dms, do_ = dense_own(torch, ops, Q, K, V, dO)
+        ref = None
+        if best:   # the fused backend timed above, never the unfused math path
+            from torch.nn.attention import sdpa_kernel
+            with sdpa_kernel([best[2]]):
+                ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True)
+        dense_mine = {"ms_per_step": round(dms, 3), "tokens_per_s": round(w.B * w.N / (dms / 1e3), 1),
+                      "lighthouse_speedup": round(dms / ms, 2),
+                      "max_abs_diff_O_vs_sdpa": (None if ref is None else
+                                                 float((do_.float() - ref.float()).abs().max())),
+                      "max_abs_O_sdpa": None if ref is None else float(ref.float().abs().max()),
+                      "what": "dense causal attention over all N tokens, forward+backward, this "
+                              "library's MFMA kernels (the layer with L=1: S=N, nothing redundant)"}
+        del do_, ref
+        print(f"[bench] dense own {dense_mine}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
@@ -328,7 +373,7 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "N": w.N, "H": w.H, "d": w.d, "p": w.p,
                    "L": w.L, "S": S, "K": w.K, "io_dtype": w.dtype, "out_dtype": w.dtype},
         "roofline": roof, "cpu_baseline": cpu, "measured_peaks": peaks, "dense_sdpa": dense,
-        "stages": stages,
+        "dense_own_kernels": dense_mine, "stages": stages,
     }
     print(json.dumps(line))
 

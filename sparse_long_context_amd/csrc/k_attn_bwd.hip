@@ -340,7 +340,8 @@ void attn_bwd_dq_kernel(
   static_assert(kQStages == 5, "block kb + 4 is issued into the slot of block kb - 1");
   extern __shared__ __align__(16) unsigned char smraw[];
   QStage<D> *stg = reinterpret_cast<QStage<D> *>(smraw);
-  uint8_t *fl_lds = smraw + sizeof(QStage<D>) * kQStages;   // flags of keys 0 .. kend-1
+  // REDUNDANT bits of keys 0 .. kend-1, one 64-bit word per 64 keys
+  uint64_t *fl_bits = reinterpret_cast<uint64_t *>(smraw + sizeof(QStage<D>) * kQStages);
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
   constexpr int L = 2 * (kQBK * D / 8 / 64) / 4;   // tile loads per wavefront per block
@@ -360,19 +361,22 @@ void attn_bwd_dq_kernel(
   const int64_t kend = min(S, (int64_t)(qb + 1) * kQBQ);
   const int nkb = (int)((kend + kQBK - 1) / kQBK);
   {
-    // flags of the workgroup's key range, 16 loads in flight per thread
-    constexpr int FPT = 16;
-    for (int64_t i0 = 0; i0 < kend; i0 += (int64_t)FPT * kQThreads) {
+    // each wavefront packs 64-key chunks with a ballot; 16 loads in flight
+    // per lane
+    constexpr int FPT = 16, WAVES = kQThreads / 64;
+    const int64_t nch = (kend + 63) / 64;
+    for (int64_t c0 = 0; c0 < nch; c0 += (int64_t)FPT * WAVES) {
       uint8_t v[FPT];
 #pragma unroll
       for (int j = 0; j < FPT; ++j) {
-        const int64_t i = i0 + (int64_t)j * kQThreads + tid;
+        const int64_t i = (c0 + (int64_t)j * WAVES + w) * 64 + lane;
         v[j] = i < kend ? flags[bh * S + i] : 0;
       }
 #pragma unroll
       for (int j = 0; j < FPT; ++j) {
-        const int64_t i = i0 + (int64_t)j * kQThreads + tid;
-        if (i < kend) fl_lds[i] = v[j];
+        const int64_t c = c0 + (int64_t)j * WAVES + w;   // uniform over the wavefront
+        const uint64_t m = __ballot((v[j] & LH_ROW_REDUNDANT) != 0);
+        if (c < nch && lane == 0) fl_bits[c] = m;
       }
     }
   }
@@ -416,7 +420,8 @@ void attn_bwd_dq_kernel(
     lds_barrier();
     if (w == 0 && lane < kQBK && kb + 1 < nkb) {
       const int64_t kk = (int64_t)(kb + 1) * kQBK + lane;
-      slot(kb + 1)->bias[lane] = (kk < kend && !(fl_lds[kk] & LH_ROW_REDUNDANT)) ? 0.f : -INFINITY;
+      const bool red = kk >= kend || ((fl_bits[kk >> 6] >> (kk & 63)) & 1u);
+      slot(kb + 1)->bias[lane] = red ? -INFINITY : 0.f;
     }
   };
   // dS^T of block kb from its S^T, dP^T (in place); EDGE: the block on the
@@ -578,8 +583,8 @@ lh_status launch_attn_bwd_dq_bf16(const Geo &g, const bf16_t *qs, const bf16_t *
                                   const float *lse, const float *drow, const uint8_t *flags,
                                   float *dqs, hipStream_t st) {
   const unsigned items = cdiv(g.S, kQBQ) * (unsigned)g.BH();
-  // LDS: the ring, then one flag byte per key of the widest key range
-  const size_t flb = (size_t)((g.S + 15) / 16 * 16);
+  // LDS: the ring, then one REDUNDANT bit per key of the widest key range
+  const size_t flb = (size_t)((g.S + 63) / 64 * 8);
 #define LH_DQ(D)                                                                              \
   do {                                                                                        \
     const size_t shm = sizeof(QStage<D>) * kQStages + flb;                                    \

@@ -70,3 +70,36 @@ def test_fullsize_layer(wid):
         print(f"[full] {w.name} head {h} {n}: max|err| {err.max():.3e}, "
               f"max|ref| {np.abs(want).max():.2f}", flush=True)
         assert np.all(err <= tol), f"{n}: exceeds tolerance by {float(np.max(err - tol)):.3e}"
+
+
+def test_dense_one_level_at_full_length():
+    """The one-level layer (L = 1: S = N, nothing redundant) is dense causal
+    attention; at N = 131072 its dQ kernel keeps the key flags of up to the
+    whole sequence in LDS.  Causality makes the outputs of the first P rows,
+    and their dQ, depend on the first P tokens alone, so the oracle checks
+    them on that prefix; the rest must be finite and deterministic."""
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dev = torch.device("cuda:0")
+    N, P = 131072, 1024
+    w = synth.Workload(0, f"dense N={N} H=1 d=128 L=1", N, 1, 128, 2, 1, N, "bf16", "bursts")
+    Q, K, V, dO = synth.make_inputs(w)
+    Qd, Kd, Vd = (x.to(dev) for x in (Q, K, V))
+    dOd = dO.to(dev, torch.bfloat16)
+    c = ops.Ctx(ops.make_dims(Qd, 2, 1, N, out_dtype=torch.bfloat16))
+    print(f"[full] dense N={N}: layer fwd+bwd", flush=True)
+    o, saved = ops.layer_fwd(c, Qd, Kd, Vd)
+    grads = ops.layer_bwd(c, saved, dOd)
+    o2, saved2 = ops.layer_fwd(c, Qd, Kd, Vd)
+    grads2 = ops.layer_bwd(c, saved2, dOd)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and all(torch.equal(a, b) for a, b in zip(grads, grads2))
+    for t in (o, *grads):
+        assert bool(torch.isfinite(t.float()).all())
+    g = orc.Geometry(P, 2, 1, 0).check()
+    fw = orc.head_forward(f64(Q[0, 0, :P]), f64(K[0, 0, :P]), f64(V[0, 0, :P]), g, store="bf16")
+    gq = orc.head_backward(fw, f64(dO[0, 0, :P]))[0]
+    for got, want, n in ((o, fw.O, "O"), (grads[0], gq, "dQ")):
+        err = np.abs(f64(got[0, 0, :P]) - want)
+        tol = 2e-2 + 0.5 * ulp_bf16(want)
+        print(f"[full] dense N={N} first {P} rows {n}: max|err| {err.max():.3e}", flush=True)
+        assert np.all(err <= tol), f"{n}: exceeds tolerance by {float(np.max(err - tol)):.3e}"
