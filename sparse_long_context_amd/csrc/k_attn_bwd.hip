@@ -57,16 +57,25 @@ struct KvStage {
 // split over the four wavefronts, plus one dword load (wavefront 0) of the
 // block's lse and drow
 template <int D>
-__device__ __forceinline__ void kv_issue(KvStage<D> &st, const bf16_t *Q, const bf16_t *DH,
-                                         const bf16_t *DL, const float *LSE, const float *DR,
-                                         int64_t q0, int64_t S, int tid) {
-  tile_load<D, kKvBQ, kKvThreads>(st.q, Q, q0, S - 1, tid);
-  tile_load<D, kKvBQ, kKvThreads>(st.dh, DH, q0, S - 1, tid);
-  tile_load<D, kKvBQ, kKvThreads>(st.dl, DL, q0, S - 1, tid);
+using KvMap = TileMap<D, kKvBQ, kKvThreads>;
+
+// rows q0 .. q0 + 31 of Q, dO hi, dO lo and their lse, D into a stage (rows
+// past S read as zeros; they are index-masked)
+template <int D>
+__device__ __forceinline__ void kv_issue(KvStage<D> &st, const KvMap<D> &map, brsrc Q, brsrc DH,
+                                         brsrc DL, brsrc LSE, brsrc DR, int64_t q0, int tid) {
+  map.load(st.q, Q, q0);
+  map.load(st.dh, DH, q0);
+  map.load(st.dl, DL, q0);
+  // wavefront 0: lanes 0-31 copy lse, lanes 32-63 drow (which follows lse);
+  // two loads, since a buffer resource is uniform over the wavefront
   if (tid < 64) {
-    const int64_t qq = min(q0 + (tid & 31), S - 1);
-    __builtin_amdgcn_global_load_lds((const void *)(tid < 32 ? LSE + qq : DR + qq),
-                                     (lds_void *)st.lse, 4, 0, 0);
+    const uint32_t qq = (uint32_t)(q0 + (tid & 31)) * 4;
+    if (tid < 32) {
+      lds_dma<4>(LSE, st.lse, qq);
+    } else {
+      lds_dma<4>(DR, st.lse, qq);
+    }
   }
 }
 
@@ -78,7 +87,7 @@ __device__ __forceinline__ void kv_wait(bool later, bool wave0) {
   if (!later) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else if (wave0) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L + 1) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L + 2) : "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
   }
@@ -108,16 +117,21 @@ void attn_bwd_dkv_kernel(
   const int64_t key = kw0 + col;
   const float sl2 = scale * kLog2e;
 
-  const bf16_t *Q = qs + bh * S * D, *DH = doh + bh * S * D, *DL = dol + bh * S * D;
-  const float *LSE = lse + bh * S, *DR = drow + bh * S;
+  const uint32_t tb = (uint32_t)(S * D * 2), sb4 = (uint32_t)(S * 4);
+  const brsrc Q = make_rsrc(qs + bh * S * D, tb), DH = make_rsrc(doh + bh * S * D, tb),
+              DL = make_rsrc(dol + bh * S * D, tb);
+  const brsrc LSE = make_rsrc(lse + bh * S, sb4), DR = make_rsrc(drow + bh * S, sb4);
   const bool dead = key >= S || (flags[bh * S + min(key, S - 1)] & LH_ROW_REDUNDANT);
   const bool all_dead = __all(dead);
 
+  KvMap<D> kmap;
+  kmap.init(tid);
   const int qb0 = (int)((int64_t)kb * kKvBK / kKvBQ);
   const int nqb = (int)((S + kKvBQ - 1) / kKvBQ);
   for (int j = 0; j < 3; ++j)
     if (qb0 + j < nqb)
-      kv_issue<D>(stg[(qb0 + j) % kKvStages], Q, DH, DL, LSE, DR, (int64_t)(qb0 + j) * kKvBQ, S, tid);
+      kv_issue<D>(stg[(qb0 + j) % kKvStages], kmap, Q, DH, DL, LSE, DR, (int64_t)(qb0 + j) * kKvBQ,
+                  tid);
 
   // K and V of this lane's key: the B operands of S = Q K^T and dP = dO V^T
   bf16x8 kreg[KSTEPS], vreg[KSTEPS];
@@ -145,44 +159,68 @@ void attn_bwd_dkv_kernel(
   };
   auto issue = [&](KvStage<D> *st, int qb) {
     if (qb + 4 < nqb)
-      kv_issue<D>(*st, Q, DH, DL, LSE, DR, (int64_t)(qb + 4) * kKvBQ, S, tid);
+      kv_issue<D>(*st, kmap, Q, DH, DL, LSE, DR, (int64_t)(qb + 4) * kKvBQ, tid);
   };
   auto slot = [&](int qb) { return &stg[(qb + kKvStages) % kKvStages]; };
   // P, dS of block qb from its S, dP (in place).  EDGE blocks (the one on
   // the wavefront's diagonal, the one crossing S) mask by index; inside the
   // range only dead keys are masked, through an infinite lse.
   const float dead_lse = dead ? INFINITY : 0.f;
-  auto softmax = [&](auto edge_tag, const KvStage<D> *sb, int qb, f32x16 &sa, f32x16 &dp) {
+  // lse and D of the block's queries 8I + 4h + J (lanes of one half share them)
+  struct RowStats { f32x4 l[4], d[4]; };
+  auto rowstats = [&](const KvStage<D> *sb, RowStats &r) {
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      r.l[I] = *reinterpret_cast<const f32x4 *>(sb->lse + 8 * I + 4 * h);
+      r.d[I] = *reinterpret_cast<const f32x4 *>(sb->drow + 8 * I + 4 * h);
+    }
+  };
+  // HALF selects the rows of one 16-query step (I = 2 HALF, 2 HALF + 1)
+  auto softmax = [&](auto edge_tag, auto half_tag, const RowStats &rs, int qb, f32x16 &sa,
+                     f32x16 &dp) {
     constexpr bool EDGE = decltype(edge_tag)::value;
+    constexpr int HALF = decltype(half_tag)::value;
     const int64_t q0 = (int64_t)qb * kKvBQ;
     const int kr = (int)(key - q0);                       // causal: query index >= kr
     const int qn = (int)min((int64_t)kKvBQ, S - q0);      // queries of the block inside S
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
+    for (int I = 2 * HALF; I < 2 * HALF + 2; ++I) {
       const int ql = 8 * I + 4 * h;
-      const f32x4 lj = *reinterpret_cast<const f32x4 *>(sb->lse + ql);
-      const f32x4 dj = *reinterpret_cast<const f32x4 *>(sb->drow + ql);
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         const int v = 4 * I + J;
         // masked entries take exp2(-inf) = 0 (selects, so the exponential
         // stays unconditional and the block stays one basic block)
-        float x = sa[v] * sl2 - (lj[J] * kLog2e + dead_lse);
+        float x = sa[v] * sl2 - (rs.l[I][J] * kLog2e + dead_lse);
         if constexpr (EDGE) x = (ql + J < kr || ql + J >= qn) ? -INFINITY : x;
         const float p = __builtin_amdgcn_exp2f(x);
         sa[v] = p;
-        dp[v] = p * (dp[v] - dj[J]);
+        dp[v] = p * (dp[v] - rs.d[I][J]);
       }
     }
   };
   // the A operands of S and dP of a block: Q, dO hi, dO lo rows
   struct RowOps { bf16x8 q[KSTEPS], dh[KSTEPS], dl[KSTEPS]; };
-  auto rowops = [&](const KvStage<D> *sb, RowOps &r) {
+  auto rows_q = [&](const KvStage<D> *sb, RowOps &r) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) r.q[s] = ld_rowop<D>(sb->q, col, s, h);
+  };
+  auto rows_d = [&](const KvStage<D> *sb, RowOps &r) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      r.q[s] = ld_rowop<D>(sb->q, col, s, h);
       r.dh[s] = ld_rowop<D>(sb->dh, col, s, h);
       r.dl[s] = ld_rowop<D>(sb->dl, col, s, h);
+    }
+  };
+  // S = Q K^T and dP = dO V^T of a block (this wavefront's 32 keys)
+  auto sdp = [&](const RowOps &r, f32x16 &sn, f32x16 &dn) {
+    sn = zero16();
+    dn = zero16();
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      sn = mfma32(r.q[s], kreg[s], sn);
+      dn = mfma32(r.dh[s], vreg[s], dn);
+      dn = mfma32(r.dl[s], vreg[s], dn);
     }
   };
   // the B operands of one 16-query step of a block: dO hi, dO lo, Q
@@ -214,6 +252,10 @@ void attn_bwd_dkv_kernel(
     }
   };
 
+  using EdgeT = std::true_type;
+  using InT = std::false_type;
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
   // first block with queries at or past this wavefront's keys
   const int f = all_dead ? nqb : (int)(kw0 / kKvBQ);
   int qb = qb0 - 1;
@@ -227,80 +269,104 @@ void attn_bwd_dkv_kernel(
       sync(qb);
       issue(slot(qb + 4), qb);
     }
-    f32x16 sa, dp;
-    RowOps ro;
+    // qb == f - 1: blocks up to f + 1 have landed.  Prologue: P, dS of
+    // block f (the diagonal, index-masked) and S, dP of block f + 1.
     sync(qb);
     issue(slot(qb + 4), qb);
-    rowops(slot(f), ro);
-    sa = zero16();
-    dp = zero16();
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      sa = mfma32(ro.q[s], kreg[s], sa);
-      dp = mfma32(ro.dh[s], vreg[s], dp);
-      dp = mfma32(ro.dl[s], vreg[s], dp);
+    f32x16 sa, dp;   // S, dP of the block whose P, dS are formed next
+    Packed k0, k1;   // P, dS of the block whose dV, dK are added next
+    ColOps c0;       // that block's first-step column operands
+    RowStats rs;     // lse, D of the block in sa, dp
+    RowOps ro;
+    rows_q(slot(f), ro);
+    rows_d(slot(f), ro);
+    sdp(ro, sa, dp);
+    rowstats(slot(f), rs);
+    softmax(EdgeT(), H0(), rs, f, sa, dp);
+    softmax(EdgeT(), H1(), rs, f, sa, dp);
+    pack(sa, dp, 0, k0);
+    pack(sa, dp, 1, k1);
+    if (f + 1 < nqb) {
+      rows_q(slot(f + 1), ro);
+      rows_d(slot(f + 1), ro);
+      sdp(ro, sa, dp);
+      rowstats(slot(f + 1), rs);
     }
-    rowops(slot(min(f + 1, nqb - 1)), ro);
-    // One steady iteration (block qb).  The slots are distinct, which the
-    // restrict qualifiers state, so the compiler does not make LDS reads
-    // wait for the global->LDS loads into `fill`; the explicit vmcnt before
-    // each barrier is what orders them.  One wavefront per SIMD: no other
-    // wavefront hides LDS latency or the VALU work, so the iteration is laid
-    // out by hand in fenced regions: (1) S and dP MFMAs of block qb + 1 (row
-    // operands read last iteration) with block qb's exponentials and splits
-    // between them, and the column operands of its first query step; (2)
-    // that step's MFMAs with the second step's reads; (3) the second step's
-    // MFMAs with the row-operand reads of block qb + 2.  Block f (the
-    // diagonal) has the index mask; later blocks up to nqb - 2 lie inside
-    // the range; block nqb - 1 goes through the tail below.
-    auto iter = [&](auto edge_tag, KvStage<D> *__restrict__ fill,
-                    const KvStage<D> *__restrict__ cur, const KvStage<D> *__restrict__ nx2) {
+    colops(slot(f), 0, c0);
+    // Steady iteration qb (f .. nqb - 3), a three-block software pipeline:
+    // dV and dK of block qb, P and dS of block qb + 1, S and dP of block
+    // qb + 2.  The parts are independent, so the exponentials and splits
+    // (VALU) run beside the dV/dK MFMAs instead of between dependent ones.
+    // The slots are distinct, which the restrict qualifiers state, so the
+    // compiler does not make LDS reads wait for the global->LDS loads into
+    // `fill`; the explicit vmcnt before each barrier is what orders them.
+    // Fenced regions with prescribed interleaves: (1) block qb's first
+    // query step (20 MFMAs) with block qb + 1's first-step exponentials and
+    // splits, and the reads of block qb's second-step columns and block
+    // qb + 2's Q rows; (2) the second step with block qb + 1's second half
+    // and the reads of block qb + 2's dO rows; (3) S and dP of block qb + 2
+    // with the reads of block qb + 1's first-step columns and block qb + 2's
+    // lse and D.  Blocks qb + 1 in this range lie inside the causal range
+    // and inside S: no index masks.
+    auto iter = [&](KvStage<D> *__restrict__ fill, const KvStage<D> *__restrict__ cur,
+                    const KvStage<D> *__restrict__ nx, const KvStage<D> *__restrict__ nx2) {
       issue(fill, qb);
-      f32x16 sn = zero16(), dn = zero16();
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        sn = mfma32(ro.q[s], kreg[s], sn);
-        dn = mfma32(ro.dh[s], vreg[s], dn);
-        dn = mfma32(ro.dl[s], vreg[s], dn);
-      }
-      softmax(edge_tag, cur, qb, sa, dp);
-      Packed k0, k1;
-      pack(sa, dp, 0, k0);
-      pack(sa, dp, 1, k1);
-      ColOps c0;
-      colops(cur, 0, c0);
       __builtin_amdgcn_sched_barrier(0);
       ColOps c1;
       colops(cur, 1, c1);
+      rows_q(nx2, ro);
+      Packed n0, n1;
       accum(k0, c0);
+      softmax(InT(), H0(), rs, qb + 1, sa, dp);
+      pack(sa, dp, 0, n0);
+      sched_mix<5 * DB, 8, (6 * DB + KSTEPS + 7) / 8, (120 + 5 * DB - 1) / (5 * DB)>();
       __builtin_amdgcn_sched_barrier(0);
-      rowops(nx2, ro);
+      rows_d(nx2, ro);
       accum(k1, c1);
-      // keeps the row-operand reads here, under the MFMAs (otherwise they
-      // sink to the top of the next iteration, where the MFMAs wait on them)
+      softmax(InT(), H1(), rs, qb + 1, sa, dp);
+      pack(sa, dp, 1, n1);
+      sched_mix<5 * DB, 8, (2 * KSTEPS + 7) / 8, (120 + 5 * DB - 1) / (5 * DB)>();
+      __builtin_amdgcn_sched_barrier(0);
+      colops(nx, 0, c0);
+      rowstats(nx2, rs);
+      sdp(ro, sa, dp);
+      sched_mix<3 * KSTEPS, 8, (6 * DB + 8 + 7) / 8, 0>();
+      pin(sa);
+      pin(dp);
+      // keeps the reads under these MFMAs (otherwise they sink to the next
+      // iteration, where their consumers would wait on them)
       asm volatile("" ::: "memory");
-      sa = sn;
-      dp = dn;
+      k0 = n0;
+      k1 = n1;
     };
-    qb = f;
-    if (qb < nqb - 1) {
+    for (qb = f; qb < nqb - 2; ++qb) {
       sync(qb);
-      iter(std::true_type(), slot(qb + 4), slot(qb), slot(min(qb + 2, nqb - 1)));
-      for (++qb; qb < nqb - 1; ++qb) {
-        sync(qb);
-        iter(std::false_type(), slot(qb + 4), slot(qb), slot(min(qb + 2, nqb - 1)));
-      }
+      iter(slot(qb + 4), slot(qb), slot(qb + 1), slot(qb + 2));
     }
-    sync(qb);   // qb == nqb - 1: nothing left to issue
-    softmax(std::true_type(), slot(qb), qb, sa, dp);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      ColOps c;
-      Packed k;
-      colops(slot(qb), s2, c);
-      pack(sa, dp, s2, k);
-      accum(k, c);
+    if (qb == nqb - 2) {
+      // dV, dK of block nqb - 2; P, dS of the last block (it may cross S:
+      // index-masked)
+      sync(qb);
+      ColOps c1;
+      colops(slot(qb), 1, c1);
+      Packed n0, n1;
+      accum(k0, c0);
+      softmax(EdgeT(), H0(), rs, qb + 1, sa, dp);
+      pack(sa, dp, 0, n0);
+      accum(k1, c1);
+      softmax(EdgeT(), H1(), rs, qb + 1, sa, dp);
+      pack(sa, dp, 1, n1);
+      colops(slot(qb + 1), 0, c0);
+      k0 = n0;
+      k1 = n1;
+      ++qb;
     }
+    // qb == nqb - 1: dV, dK of the last block
+    sync(qb);
+    ColOps c1;
+    colops(slot(qb), 1, c1);
+    accum(k0, c0);
+    accum(k1, c1);
   }
 
   // lane: head-dim column b*32 + col; rows are keys kw0 + 8I + 4h + J
@@ -356,7 +422,8 @@ void attn_bwd_dq_kernel(
   const int64_t q0w = (int64_t)qb * kQBQ + w * 32;
   const int64_t q = q0w + col;
   const float sl2 = scale * kLog2e;
-  const bf16_t *Kg = ks + bh * S * D, *Vg = vs + bh * S * D;
+  const brsrc Kg = make_rsrc(ks + bh * S * D, (uint32_t)(S * D * 2)),
+              Vg = make_rsrc(vs + bh * S * D, (uint32_t)(S * D * 2));
 
   const int64_t kend = min(S, (int64_t)(qb + 1) * kQBQ);
   const int nkb = (int)((kend + kQBK - 1) / kQBK);
@@ -399,10 +466,12 @@ void attn_bwd_dq_kernel(
   // the loop (otherwise it re-waits for them inside every iteration)
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
+  TileMap<D, kQBK, kQThreads> qmap;
+  qmap.init(tid);
   auto issue = [&](QStage<D> *st, int kb) {   // block kb + 4 into st
     if (kb + 4 < nkb) {
-      tile_load<D, kQBK, kQThreads>(st->k, Kg, (int64_t)(kb + 4) * kQBK, S - 1, tid);
-      tile_load<D, kQBK, kQThreads>(st->v, Vg, (int64_t)(kb + 4) * kQBK, S - 1, tid);
+      qmap.load(st->k, Kg, (int64_t)(kb + 4) * kQBK);   // rows past S read as zeros (masked)
+      qmap.load(st->v, Vg, (int64_t)(kb + 4) * kQBK);
     }
   };
   auto slot = [&](int kb) { return &stg[(kb + kQStages) % kQStages]; };
@@ -563,6 +632,7 @@ lh_status launch_attn_bwd_dkv_bf16(const Geo &g, const bf16_t *qs, const bf16_t 
                                    const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
                                    const float *lse, const float *drow, const uint8_t *flags,
                                    float *dks, float *dvs, hipStream_t st) {
+  if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
   const unsigned items = cdiv(g.S, kKvBK) * (unsigned)g.BH();
 #define LH_DKV(D)                                                                             \
   do {                                                                                        \
@@ -582,6 +652,7 @@ lh_status launch_attn_bwd_dq_bf16(const Geo &g, const bf16_t *qs, const bf16_t *
                                   const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
                                   const float *lse, const float *drow, const uint8_t *flags,
                                   float *dqs, hipStream_t st) {
+  if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
   const unsigned items = cdiv(g.S, kQBQ) * (unsigned)g.BH();
   // LDS: the ring, then one REDUNDANT bit per key of the widest key range
   const size_t flb = (size_t)((g.S + 63) / 64 * 8);

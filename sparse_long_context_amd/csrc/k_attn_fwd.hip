@@ -26,7 +26,7 @@
 // is only moved (and O, l rescaled) when a row's maximum grows by more than
 // 2^8, which keeps P <= 256.
 //
-// Tiles reach LDS by direct global->LDS loads (global_load_lds_dwordx4),
+// Tiles reach LDS by direct buffer->LDS loads (buffer_load_dwordx4 ... lds),
 // double-buffered, in an XOR-swizzled layout (no padding) that keeps the
 // MFMA operand reads free of bank conflicts.
 #include "lh_mfma.h"
@@ -75,8 +75,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   const int64_t q = q0w + col;
 
   const bf16_t *Q = qs + bh * S * D;
-  const bf16_t *Kg = ks + bh * S * D;
-  const bf16_t *Vt = vst + bh * (int64_t)D * Sp;
+  const brsrc Kg = make_rsrc(ks + bh * S * D, (uint32_t)(S * D * 2));
+  const brsrc Vt = make_rsrc(vst + bh * (int64_t)D * Sp, (uint32_t)(D * Sp * 2));
   const uint8_t *fl = flags + bh * S;
 
   bf16x8 qreg[KSTEPS];
@@ -102,16 +102,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
       const int r = chunk / (D / 8), p = chunk % (D / 8);                                     \
       const int c = p ^ swz_k<D>(r);                                                          \
       const int64_t key = min(k0_ + r, S - 1);     /* rows past S: -inf bias */               \
-      __builtin_amdgcn_global_load_lds((const void *)(Kg + key * D + c * 8),                  \
-                                       (lds_void *)(kdst + j * 1024), 16, 0, 0);              \
+      lds_dma<16>(Kg, kdst + j * 1024, (uint32_t)((key * D + c * 8) * 2));                    \
     }                                                                                         \
     _Pragma("unroll") for (int i = 0; i < VLOADS; ++i) {                                     \
       const int j = wg * VLOADS + i;                                                          \
       const int chunk = j * 64 + lane;                                                        \
       const int dd = chunk / 8, p = chunk % 8;                                                \
       const int c = p ^ swz_v(dd);                                                            \
-      __builtin_amdgcn_global_load_lds((const void *)(Vt + (int64_t)dd * Sp + k0_ + c * 8),   \
-                                       (lds_void *)(vdst + j * 1024), 16, 0, 0);              \
+      lds_dma<16>(Vt, vdst + j * 1024, (uint32_t)(((int64_t)dd * Sp + k0_ + c * 8) * 2));      \
     }                                                                                         \
   } while (0)
 #define LH_FWD_BIAS(kb_)                                                                      \
@@ -267,6 +265,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
 lh_status launch_attn_fwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                const bf16_t *vst, const uint8_t *flags, float *os, float *lse,
                                hipStream_t st) {
+  if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
   const unsigned items = cdiv(g.S, kFwdBM) * (unsigned)g.BH();
   const float sl2 = g.scale * 1.4426950408889634f;
   if (g.d == 128) {

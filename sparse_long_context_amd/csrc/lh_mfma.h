@@ -128,28 +128,104 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// async global -> LDS copy of ROWS rows of a [*, D] bf16 matrix (row stride
-// D) into a swizzled row tile, by the NTHR threads t = 0..NTHR-1 (whole
-// wavefronts, each issuing the same number of 1 KB pieces); rows past `rmax`
-// repeat row rmax
-template <int D, int ROWS, int NTHR>
-__device__ __forceinline__ void tile_load(bf16_t *dst, const bf16_t *src, int64_t row0,
-                                          int64_t rmax, int t) {
-  constexpr int PIECES = ROWS * D / 8 / 64;
-  constexpr int WAVES = NTHR / 64;
-  static_assert(PIECES % WAVES == 0, "pieces split evenly over the wavefronts");
-  const int lane = t & 63, w = t >> 6;
+// An accumulator tile "used" at this point: the MFMAs that form it cannot
+// be moved below here by code motion (a scheduling fence alone does not stop
+// it).  Emits nothing.
+__device__ __forceinline__ void pin(const f32x16 &x) { asm volatile("" ::"a"(x)); }
+
+// Issue-order prescriptions for the scheduler, within one fenced region:
+// NM times one MFMA followed by NR LDS reads (reads started early, under
+// MFMAs that do not need them), or by NV VALU instructions (transcendentals
+// included).  Groups the region cannot fill are skipped.
+template <int NM, int NR>
+__device__ __forceinline__ void sched_mfma_reads() {
 #pragma unroll
-  for (int i = 0; i < PIECES / WAVES; ++i) {
-    const int j = w + i * WAVES;
-    const int chunk = j * 64 + lane;
-    const int r = chunk / (D / 8), p = chunk % (D / 8);
-    const int c = p ^ swz_r<D>(r);
-    const int64_t row = min(row0 + r, rmax);
-    __builtin_amdgcn_global_load_lds((const void *)(src + row * D + c * 8),
-                                     (lds_void *)(reinterpret_cast<unsigned char *>(dst) + j * 1024),
-                                     16, 0, 0);
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);   // DS read
   }
 }
+// NM MFMAs, the first RG of them each followed by NR LDS reads, every one
+// followed by NV VALU instructions (NV = 0: VALU left unconstrained)
+template <int NM, int RG, int NR, int NV>
+__device__ __forceinline__ void sched_mix() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < RG) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);
+  }
+}
+template <int NM, int NV>
+__device__ __forceinline__ void sched_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);   // VALU and transcendental
+  }
+}
+
+// Raw buffer resource over `nbytes` bytes at `p` (word 3: 32-bit data
+// format, as gfx9 raw buffer accesses require).  Global->LDS copies go
+// through buffer loads rather than global (FLAT) loads: an outstanding FLAT
+// load that writes LDS makes the compiler treat the LDS counter as out of
+// order and wait for every LDS read at the first use of any of them, while
+// buffer loads leave LDS reads counted in order.  Loads past `nbytes` read
+// zeros.
+typedef __amdgpu_buffer_rsrc_t brsrc;
+__device__ __forceinline__ brsrc make_rsrc(const void *p, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)nbytes,
+                                           0x00020000);
+}
+// one head's subsequence rows (S x d) and its transposed copy (d x Sp) in
+// bf16 fit a buffer resource's 31-bit byte range
+inline bool rsrc_fits(const Geo &g) {
+  return (int64_t)g.S * g.d * 2 <= INT32_MAX && (int64_t)g.Sp * g.d * 2 <= INT32_MAX;
+}
+// async copy of `bytes` (4 or 16) at byte offset `off` of `r` into LDS at
+// `dst` + 4 or 16 x lane (dst uniform over the wavefront)
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(brsrc r, void *dst, uint32_t off) {
+  static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte pieces");
+  if constexpr (BYTES == 16) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, off, 0, 0, 0);
+  }
+}
+
+// Async global -> LDS copies of ROWS-row blocks of a [*, D] bf16 matrix
+// (row stride D, read through a buffer resource) into swizzled row tiles,
+// by the NTHR threads t = 0..NTHR-1 (whole wavefronts, each issuing the same
+// number of 1 KB pieces).  The per-thread source offsets within a block are
+// fixed, so they are computed once; a block then costs one add per piece.
+// Rows past the resource's end read as zeros.
+template <int D, int ROWS, int NTHR>
+struct TileMap {
+  static constexpr int WAVES = NTHR / 64;
+  static constexpr int PIECES = ROWS * D / 8 / 64;
+  static_assert(PIECES % WAVES == 0, "pieces split evenly over the wavefronts");
+  static constexpr int NP = PIECES / WAVES;
+  uint32_t off[NP];   // byte offset of this thread's 16 bytes of piece i
+  int w;              // wavefront index (uniform)
+  __device__ __forceinline__ void init(int t) {
+    const int lane = t & 63;
+    w = __builtin_amdgcn_readfirstlane(t >> 6);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int chunk = (w + i * WAVES) * 64 + lane;
+      const int r = chunk / (D / 8), p = chunk % (D / 8);
+      off[i] = (uint32_t)((r * D + (p ^ swz_r<D>(r)) * 8) * 2);
+    }
+  }
+  // rows row0 .. row0 + ROWS - 1 of `src` into the tile at `dst`
+  __device__ __forceinline__ void load(bf16_t *dst, brsrc src, int64_t row0) const {
+    const uint32_t base = (uint32_t)(row0 * D * 2);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      lds_dma<16>(src, reinterpret_cast<unsigned char *>(dst) + (w + i * WAVES) * 1024,
+                  base + off[i]);
+  }
+};
 
 }  // namespace lh
