@@ -480,32 +480,45 @@ void attn_bwd_dq_kernel(
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc_dq[b] = zero16();
 
+  // bias (0, or -inf for a redundant key or one past the range) of key
+  // block kb, written into its slot by wavefront 0
+  auto write_bias = [&](int kb) {
+    if (w == 0 && lane < kQBK && kb < nkb) {
+      const int64_t kk = (int64_t)kb * kQBK + lane;
+      const bool red = kk >= kend || ((fl_bits[kk >> 6] >> (kk & 63)) & 1u);
+      slot(kb)->bias[lane] = red ? -INFINITY : 0.f;
+    }
+  };
   // Iteration kb (-1 .. nkb - 1) waits for block kb + 2, has wavefront 0
-  // turn block kb + 1's flags into its bias slot, and issues block kb + 4
-  // into the slot of block kb - 1.
+  // write block kb + 2's bias (read after the next barrier), and issues
+  // block kb + 4 into the slot of block kb - 1.
   auto sync = [&](int kb) {
     if (kb + 3 >= nkb) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
     lds_barrier();
-    if (w == 0 && lane < kQBK && kb + 1 < nkb) {
-      const int64_t kk = (int64_t)(kb + 1) * kQBK + lane;
-      const bool red = kk >= kend || ((fl_bits[kk >> 6] >> (kk & 63)) & 1u);
-      slot(kb + 1)->bias[lane] = red ? -INFINITY : 0.f;
-    }
+    write_bias(kb + 2);
   };
-  // dS^T of block kb from its S^T, dP^T (in place); EDGE: the block on the
-  // wavefront's diagonal (keys past the query masked)
-  auto softmax = [&](auto edge_tag, const QStage<D> *sb, int kb, f32x16 &sa, f32x16 &dp) {
+  // the bias of a block's keys 8I + 4h + J (lanes of one half share them)
+  struct Bias { f32x4 b[4]; };
+  auto biases = [&](const QStage<D> *sb, Bias &r) {
+#pragma unroll
+    for (int I = 0; I < 4; ++I) r.b[I] = *reinterpret_cast<const f32x4 *>(sb->bias + 8 * I + 4 * h);
+  };
+  // dS^T of block kb from its S^T, dP^T (in place), for the keys of one
+  // 16-key step (HALF); EDGE: the block on the wavefront's diagonal (keys
+  // past the query masked)
+  auto softmax = [&](auto edge_tag, auto half_tag, const Bias &bs, int kb, f32x16 &sa,
+                     f32x16 &dp) {
     constexpr bool EDGE = decltype(edge_tag)::value;
+    constexpr int HALF = decltype(half_tag)::value;
     const int qr = (int)(q - (int64_t)kb * kQBK);   // causal: key index <= qr
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
+    for (int I = 2 * HALF; I < 2 * HALF + 2; ++I) {
       const int kl = 8 * I + 4 * h;
-      const f32x4 bj = *reinterpret_cast<const f32x4 *>(sb->bias + kl);
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         const int v = 4 * I + J;
-        float x = sa[v] * sl2 + (bj[J] - lse2);
+        float x = sa[v] * sl2 + (bs.b[I][J] - lse2);
         if constexpr (EDGE) x = kl + J > qr ? -INFINITY : x;
         const float p = __builtin_amdgcn_exp2f(x);
         dp[v] = p * (dp[v] - dr);
@@ -514,11 +527,23 @@ void attn_bwd_dq_kernel(
   };
   // the A operands of S^T and dP^T of a block: K and V rows
   struct RowOps { bf16x8 k[KSTEPS], v[KSTEPS]; };
-  auto rowops = [&](const QStage<D> *sb, RowOps &r) {
+  auto rows_k = [&](const QStage<D> *sb, RowOps &r) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) r.k[s] = ld_rowop<D>(sb->k, col, s, h);
+  };
+  auto rows_v = [&](const QStage<D> *sb, RowOps &r) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) r.v[s] = ld_rowop<D>(sb->v, col, s, h);
+  };
+  // S^T = K Q^T and dP^T = V dO^T of a block (this wavefront's 32 queries)
+  auto sdp = [&](const RowOps &r, f32x16 &sn, f32x16 &dn) {
+    sn = zero16();
+    dn = zero16();
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      r.k[s] = ld_rowop<D>(sb->k, col, s, h);
-      r.v[s] = ld_rowop<D>(sb->v, col, s, h);
+      sn = mfma32(r.k[s], qreg[s], sn);
+      dn = mfma32(r.v[s], dregh[s], dn);
+      dn = mfma32(r.v[s], dregl[s], dn);
     }
   };
   // the A operands of one 16-key step: K^T through the transposing read
@@ -534,7 +559,13 @@ void attn_bwd_dq_kernel(
       acc_dq[b] = mfma32(a[b], bsl, acc_dq[b]);
     }
   };
+  using EdgeT = std::true_type;
+  using InT = std::false_type;
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
 
+  // block 0's bias is needed right after the first barrier
+  write_bias(0);
   // last key block of this wavefront (its diagonal, or the last one of S)
   const int lw = q0w < S ? (int)min((int64_t)nkb - 1, (q0w + 31) / kQBK) : -1;
   int kb = -1;
@@ -544,65 +575,108 @@ void attn_bwd_dq_kernel(
       issue(slot(kb + 4), kb);
     }
   } else {
-    f32x16 sa, dp;
-    RowOps ro;
+    // kb == -1: blocks 0 and 1 have landed.  Prologue: dS of block 0 and
+    // S, dP of block 1.
     sync(kb);
     issue(slot(kb + 4), kb);
-    rowops(slot(0), ro);
-    sa = zero16();
-    dp = zero16();
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      sa = mfma32(ro.k[s], qreg[s], sa);
-      dp = mfma32(ro.v[s], dregh[s], dp);
-      dp = mfma32(ro.v[s], dregl[s], dp);
+    f32x16 sa, dp;               // S^T, dP^T of the block whose dS is formed next
+    bf16x8 h0, l0, h1, l1;       // dS^T split of the block whose dQ is added next
+    bf16x8 a0[DB];               // that block's first-step K^T operands
+    Bias bs;                     // bias of the block in sa, dp
+    RowOps ro;
+    rows_k(slot(0), ro);
+    rows_v(slot(0), ro);
+    sdp(ro, sa, dp);
+    biases(slot(0), bs);
+    if (lw == 0) {
+      softmax(EdgeT(), H0(), bs, 0, sa, dp);
+      softmax(EdgeT(), H1(), bs, 0, sa, dp);
+    } else {
+      softmax(InT(), H0(), bs, 0, sa, dp);
+      softmax(InT(), H1(), bs, 0, sa, dp);
     }
-    rowops(slot(min(1, nkb - 1)), ro);
-    // steady iterations (block kb), laid out as in the dK/dV kernel: S^T,
-    // dP^T of block kb + 1 from row operands read last iteration, with block
-    // kb's exponentials and splits between them; then the dQ MFMAs, with
-    // block kb + 2's row-operand reads under the last ones.  The restrict
-    // qualifiers state that the slots are distinct.
+    pack_split(dp, 0, h0, l0);
+    pack_split(dp, 8, h1, l1);
+    if (lw >= 1) {
+      rows_k(slot(1), ro);
+      rows_v(slot(1), ro);
+      sdp(ro, sa, dp);
+    }
+    colops(slot(0), 0, a0);
+    // Steady iteration kb (0 .. lw - 2), a three-block software pipeline
+    // as in the dK/dV kernel: dQ of block kb, dS of block kb + 1 (inside
+    // the causal range: no index mask), S and dP of block kb + 2.  Fenced
+    // regions: (1) block kb's first key step (8 MFMAs) with block kb + 1's
+    // first-half exponentials and split, and the reads of block kb's
+    // second-step K^T, block kb + 2's K rows and block kb + 1's bias; (2)
+    // the second step with block kb + 1's second half and the reads of
+    // block kb + 2's V rows; (3) S and dP of block kb + 2 with the reads of
+    // block kb + 1's first-step K^T.  The restrict qualifiers state that the
+    // slots are distinct.
     auto iter = [&](QStage<D> *__restrict__ fill, const QStage<D> *__restrict__ cur,
-                    const QStage<D> *__restrict__ nx2) {
+                    const QStage<D> *__restrict__ nx, const QStage<D> *__restrict__ nx2) {
       issue(fill, kb);
-      f32x16 sn = zero16(), dn = zero16();
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        sn = mfma32(ro.k[s], qreg[s], sn);
-        dn = mfma32(ro.v[s], dregh[s], dn);
-        dn = mfma32(ro.v[s], dregl[s], dn);
-      }
-      softmax(std::false_type(), cur, kb, sa, dp);
-      bf16x8 h0, l0, h1, l1;
-      pack_split(dp, 0, h0, l0);
-      pack_split(dp, 8, h1, l1);
-      bf16x8 a0[DB];
-      colops(cur, 0, a0);
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 a1[DB];
       colops(cur, 1, a1);
+      biases(nx, bs);
+      rows_k(nx2, ro);
+      bf16x8 nh0, nl0, nh1, nl1;
       accum(h0, l0, a0);
+      softmax(InT(), H0(), bs, kb + 1, sa, dp);
+      pack_split(dp, 0, nh0, nl0);
+      sched_mix<2 * DB, 2 * DB, (2 * DB + 4 + KSTEPS + 2 * DB - 1) / (2 * DB),
+                (110 + 2 * DB - 1) / (2 * DB)>();
       __builtin_amdgcn_sched_barrier(0);
-      rowops(nx2, ro);
+      rows_v(nx2, ro);
       accum(h1, l1, a1);
-      asm volatile("" ::: "memory");   // keeps the row-operand reads under the MFMAs
-      sa = sn;
-      dp = dn;
+      softmax(InT(), H1(), bs, kb + 1, sa, dp);
+      pack_split(dp, 8, nh1, nl1);
+      sched_mix<2 * DB, 2 * DB, (KSTEPS + 2 * DB - 1) / (2 * DB), (110 + 2 * DB - 1) / (2 * DB)>();
+      __builtin_amdgcn_sched_barrier(0);
+      colops(nx, 0, a0);
+      sdp(ro, sa, dp);
+      sched_mix<3 * KSTEPS, 8, (2 * DB + 7) / 8, 0>();
+      pin(sa);
+      pin(dp);
+      asm volatile("" ::: "memory");   // keeps the reads under these MFMAs
+      h0 = nh0;
+      l0 = nl0;
+      h1 = nh1;
+      l1 = nl1;
     };
-    for (kb = 0; kb < lw; ++kb) {
+    for (kb = 0; kb < lw - 1; ++kb) {
       sync(kb);
-      iter(slot(kb + 4), slot(kb), slot(min(kb + 2, nkb - 1)));
+      iter(slot(kb + 4), slot(kb), slot(kb + 1), slot(kb + 2));
     }
-    sync(kb);   // kb == lw: the diagonal block
+    if (kb == lw - 1) {
+      // dQ of block lw - 1; dS of the diagonal block lw
+      sync(kb);
+      issue(slot(kb + 4), kb);
+      bf16x8 a1[DB], nh0, nl0, nh1, nl1;
+      colops(slot(kb), 1, a1);
+      biases(slot(kb + 1), bs);
+      accum(h0, l0, a0);
+      softmax(EdgeT(), H0(), bs, kb + 1, sa, dp);
+      pack_split(dp, 0, nh0, nl0);
+      accum(h1, l1, a1);
+      softmax(EdgeT(), H1(), bs, kb + 1, sa, dp);
+      pack_split(dp, 8, nh1, nl1);
+      colops(slot(kb + 1), 0, a0);
+      h0 = nh0;
+      l0 = nl0;
+      h1 = nh1;
+      l1 = nl1;
+      ++kb;
+    }
+    // kb == lw: dQ of the diagonal block
+    sync(kb);
     issue(slot(kb + 4), kb);
-    softmax(std::true_type(), slot(kb), kb, sa, dp);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 a[DB], bh_, bl_;
-      colops(slot(kb), s2, a);
-      pack_split(dp, 8 * s2, bh_, bl_);
-      accum(bh_, bl_, a);
+    {
+      bf16x8 a1[DB];
+      colops(slot(kb), 1, a1);
+      accum(h0, l0, a0);
+      accum(h1, l1, a1);
     }
     for (++kb; kb < nkb; ++kb) {
       sync(kb);

@@ -76,15 +76,24 @@ __device__ __forceinline__ void pack_split(const f32x16 &acc, int o, bf16x8 &hi,
 // the 8-byte pieces addressed by lanes a, a+4, a+8, a+12 of that group, so a
 // group whose lane j points at row kbase + j/4, columns n0 + 4(j%4) receives
 // column n0 + i of rows kbase..kbase+3 in its lane i.  16-byte chunks are
-// XOR-swizzled per row so that both reads stay free of bank conflicts.
+// XOR-swizzled per row (swz_r) so that both reads stay free of bank
+// conflicts.
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+// Chunk permutation of row r.  LDS serves a 16-byte-per-lane read in
+// passes of 16 lanes and the 8-byte transposing read in passes of 32 lanes
+// (64 banks of 4 bytes).  A row-operand pass reads one chunk of each of 16
+// consecutive rows; a transposing pass reads four consecutive chunks of each
+// of 4 consecutive rows.  D = 128 (a row spans all banks): the low two row
+// bits pick the 4-chunk group, bits 2-3 the chunk inside it, so both passes
+// touch 16 distinct chunks.  D = 64 (two rows per bank line): row bit 1
+// picks the group and bits 1-3 of the row, reversed, make rows of one parity
+// distinct.
 template <int D>
 __device__ __forceinline__ int swz_r(int r) {
-  int f = ((r & 3) << 1) | ((r >> 2) & 1);
-  if (D == 128) f |= ((r >> 3) & 1) << 3;
-  return f;
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
 }
 // element offset of (row r, column n) in a swizzled row tile
 template <int D>
