@@ -307,11 +307,11 @@ def main():
 
         r["pq"], r["pk"], r["pv"], r["sq"], r["sk"] = timed("pyramid_score", lambda: ops.pyramid_score(c, Q, K, V))
         r["idx"], r["anc"], r["fl"], r["row_of"] = timed("topk_select", lambda: ops.topk_select(c, r["sq"], r["sk"]))
-        r["qs"], r["ks"], r["vs"], r["qst"], r["kst"], r["vst"] = timed(
-            "gather", lambda: ops.gather(c, Q, K, V, r["pq"], r["pk"], r["pv"], r["idx"], transposed=True))
+        r["qs"], r["ks"], r["vs"] = timed(
+            "gather", lambda: ops.gather(c, Q, K, V, r["pq"], r["pk"], r["pv"], r["idx"]))
         os_ = torch.empty(w.B, w.H, S, w.d, dtype=torch.float32, device=dev)
         lse = torch.empty(w.B, w.H, S, dtype=torch.float32, device=dev)
-        timed("attn_fwd_mfma", lambda: ops.attn_fwd_mfma(c, r["qs"], r["ks"], r["vst"], r["fl"], os_, lse))
+        timed("attn_fwd_mfma", lambda: ops.attn_fwd_mfma(c, r["qs"], r["ks"], r["vs"], r["fl"], os_, lse))
         timed("scatter", lambda: ops.scatter(c, os_, r["anc"], r["fl"]))
         dos = timed("scatter_bwd", lambda: ops.scatter_bwd(c, dO, r["anc"], r["fl"]))
         hi, lo, drow = timed("attn_bwd_prep", lambda: ops.attn_bwd_prep(c, dos, os_))

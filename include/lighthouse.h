@@ -113,12 +113,9 @@ typedef struct lh_dims {
  *   row_of       [B,H,E]     int32     subsequence row of each entry, -1 if
  *                                      unselected
  *   qs, ks, vs   [B,H,S,d]   io_dtype  gathered subsequence
- *   vst          [B,H,d,Sp]  io_dtype  transposed copy of vs (LH_BF16 I/O;
- *                                      NULL for LH_F32)
- *   qst, kst                           unused by the layer calls (may be
+ *   qst, kst, vst                      unused by the layer calls (may be
  *                                      NULL); kept so callers can hold the
- *                                      other transposed copies lh_gather
- *                                      writes
+ *                                      transposed copies lh_gather writes
  *   os           [B,H,S,d]   float32   subsequence attention output (kept
  *                                      in float32: the backward's
  *                                      rowsum(dOS * OS) needs it unrounded)
@@ -226,7 +223,7 @@ lh_status lh_gather(const lh_dims *dims, const void *q, const void *k,
  * denominator (natural log, scaled logits).  os is float32 [B,H,S,d].
  * bf16 I/O runs on MFMA with float32 accumulation; f32 I/O runs on the
  * vector ALUs with float64 sums.
- * Workspace: sizes.ws_attn_fwd bytes (the transposed copy of vs). */
+ * Workspace: sizes.ws_attn_fwd bytes (0: ws may be NULL). */
 lh_status lh_subseq_attn_fwd(const lh_dims *dims, const void *qs,
                              const void *ks, const void *vs,
                              const uint8_t *sel_flags, void *os, float *lse,
@@ -246,18 +243,18 @@ lh_status lh_subseq_attn_bwd(const lh_dims *dims, const void *qs,
  * launches exactly one kernel (LH_BF16 I/O only; LH_ERR_UNSUPPORTED
  * otherwise).  They take the operand layouts the kernels read directly, for
  * callers that keep those buffers themselves, and for per-kernel timing.
- *   vst                   [B,H,d,Sp] bf16 transposed copy of vs (zero padding)
  *   dos_hi, dos_lo        [B,H,S,d]  bf16 two-term split of dOS (hi + lo)
  *   drow                  [B,H,S]    float32 rowsum(dOS * OS)
  * lh_attn_bwd_prep:     dos (float32 [B,H,S,d]) and os (float32) -> dos_hi,
  *                       dos_lo, drow
- * lh_attn_fwd_mfma:     os [B,H,S,d] float32, lse [B,H,S] (as lh_subseq_attn_fwd)
+ * lh_attn_fwd_mfma:     qs, ks, vs rows -> os [B,H,S,d] float32, lse [B,H,S]
+ *                       (as lh_subseq_attn_fwd)
  * lh_attn_bwd_dkv_mfma: dks, dvs [B,H,S,d] float32
  * lh_attn_bwd_dq_mfma:  dqs [B,H,S,d] float32 */
 lh_status lh_attn_bwd_prep(const lh_dims *dims, const float *dos, const float *os,
                            void *dos_hi, void *dos_lo, float *drow, lh_stream stream);
 lh_status lh_attn_fwd_mfma(const lh_dims *dims, const void *qs, const void *ks,
-                           const void *vst, const uint8_t *sel_flags, float *os,
+                           const void *vs, const uint8_t *sel_flags, float *os,
                            float *lse, lh_stream stream);
 lh_status lh_attn_bwd_dkv_mfma(const lh_dims *dims, const void *qs, const void *ks,
                                const void *vs, const void *dos_hi, const void *dos_lo,
@@ -315,7 +312,7 @@ lh_status lh_gather_bwd(const lh_dims *dims, const float *dqs,
                         lh_stream stream);
 
 /* ---- whole layer ----
- * Forward: pyramid+score, select, gather (+ transposed copies), attention,
+ * Forward: pyramid+score, select, gather, attention,
  * scatter (causal hold, or span broadcast per dims->scatter_mode).  Fills
  * every buffer of *saved and o [B,H,N,d] out_dtype.
  * Workspace: sizes.ws_layer_fwd bytes (may be 0 / NULL when that is 0; the

@@ -63,22 +63,19 @@ lh_status make_geo(const lh_dims *dm, Geo *g) {
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Sizes {
-  size_t subseq, subseq_t, rowf32, subseq_f32, drow;
+  size_t subseq, rowf32, subseq_f32, drow;
 };
 
 static Sizes sizes_of(const Geo &g) {
   Sizes z;
   const size_t bh = (size_t)g.BH();
   z.subseq = bh * g.S * g.d * el_size(g.io);
-  z.subseq_t = bh * g.d * g.Sp * 2;
   z.subseq_f32 = bh * g.S * g.d * 4;
   z.drow = bh * g.S * 4;
   return z;
 }
 
-static size_t ws_attn_fwd(const Geo &g) {
-  return g.io == LH_BF16 ? al256(sizes_of(g).subseq_t) : 0;
-}
+static size_t ws_attn_fwd(const Geo &) { return 0; }
 static size_t rows_bf16(const Geo &g) { return (size_t)g.BH() * g.S * g.d * 2; }
 static size_t ws_attn_bwd(const Geo &g) {
   Sizes z = sizes_of(g);
@@ -262,10 +259,9 @@ lh_status lh_subseq_attn_fwd(const lh_dims *dims, const void *qs, const void *ks
   if (g.io == LH_F32)
     return launch_attn_fwd_f32(g, (const float *)qs, (const float *)ks, (const float *)vs,
                                sel_flags, (float *)os, lse, st);
-  const size_t need = ws_attn_fwd(g);
-  if (ws_bytes < need || !ws || !aligned16(ws)) return LH_ERR_WORKSPACE;
-  LH_TRY(launch_transpose(g, vs, ws, st));
-  return launch_attn_fwd_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)ws,
+  (void)ws;
+  (void)ws_bytes;
+  return launch_attn_fwd_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
                               sel_flags, (float *)os, lse, st);
 }
 
@@ -310,14 +306,14 @@ lh_status lh_attn_bwd_prep(const lh_dims *dims, const float *dos, const float *o
                          (hipStream_t)stream);
 }
 
-lh_status lh_attn_fwd_mfma(const lh_dims *dims, const void *qs, const void *ks, const void *vst,
+lh_status lh_attn_fwd_mfma(const lh_dims *dims, const void *qs, const void *ks, const void *vs,
                            const uint8_t *sel_flags, float *os, float *lse, lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
   if (g.io != LH_BF16) return LH_ERR_UNSUPPORTED;
-  LH_REQ(qs && ks && vst && sel_flags && os && lse);
-  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vst) && aligned16(os) && aligned4(lse));
-  return launch_attn_fwd_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vst,
+  LH_REQ(qs && ks && vs && sel_flags && os && lse);
+  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(os) && aligned4(lse));
+  return launch_attn_fwd_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
                               sel_flags, os, lse, (hipStream_t)stream);
 }
 
@@ -422,7 +418,6 @@ static lh_status check_saved(const Geo &g, const lh_saved *s) {
          aligned4(s->sk) && aligned4(s->sel_idx) && aligned4(s->sel_anchor) &&
          aligned4(s->row_of) && aligned16(s->qs) && aligned16(s->ks) && aligned16(s->vs) &&
          aligned16(s->os) && aligned4(s->lse));
-  if (g.io == LH_BF16) LH_REQ(s->vst && aligned16(s->vst));
   return LH_OK;
 }
 
@@ -441,10 +436,10 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
   LH_TRY(launch_select(g, s->sq, s->sk, s->sel_idx, s->sel_anchor, s->sel_flags, s->row_of, st));
   const bool bf = g.io == LH_BF16;
   LH_TRY(gather_impl(g, q, k, v, s->pq, s->pk, s->pv, s->sel_idx, s->qs, s->ks, s->vs, nullptr,
-                     nullptr, bf ? s->vst : nullptr, st));
+                     nullptr, nullptr, st));
   if (bf)
     LH_TRY(launch_attn_fwd_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
-                                (const bf16_t *)s->vst, s->sel_flags, (float *)s->os, s->lse,
+                                (const bf16_t *)s->vs, s->sel_flags, (float *)s->os, s->lse,
                                 st));
   else
     LH_TRY(launch_attn_fwd_f32(g, (const float *)s->qs, (const float *)s->ks,

@@ -388,12 +388,9 @@ constexpr int kQBK = 32;       // keys per block
 constexpr int kQThreads = 256;
 constexpr int kQStages = 5;    // LDS ring: three blocks resident, two loading
 
+static_assert(kQBK == kKeyBlock, "dQ streams the shared key blocks");
 template <int D>
-struct QStage {
-  bf16_t k[kQBK * D];   // K rows of the block
-  bf16_t v[kQBK * D];   // V rows
-  float bias[kQBK];     // 0, or -inf for a redundant key or one past S
-};
+using QStage = KeyStage<D>;
 
 template <int D>
 __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -427,26 +424,7 @@ void attn_bwd_dq_kernel(
 
   const int64_t kend = min(S, (int64_t)(qb + 1) * kQBQ);
   const int nkb = (int)((kend + kQBK - 1) / kQBK);
-  {
-    // each wavefront packs 64-key chunks with a ballot; 16 loads in flight
-    // per lane
-    constexpr int FPT = 16, WAVES = kQThreads / 64;
-    const int64_t nch = (kend + 63) / 64;
-    for (int64_t c0 = 0; c0 < nch; c0 += (int64_t)FPT * WAVES) {
-      uint8_t v[FPT];
-#pragma unroll
-      for (int j = 0; j < FPT; ++j) {
-        const int64_t i = (c0 + (int64_t)j * WAVES + w) * 64 + lane;
-        v[j] = i < kend ? flags[bh * S + i] : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < FPT; ++j) {
-        const int64_t c = c0 + (int64_t)j * WAVES + w;   // uniform over the wavefront
-        const uint64_t m = __ballot((v[j] & LH_ROW_REDUNDANT) != 0);
-        if (c < nch && lane == 0) fl_bits[c] = m;
-      }
-    }
-  }
+  stage_flag_bits<kQThreads>(fl_bits, flags + bh * S, kend, w, lane);
 
   // this lane's query: Q and dO (hi, lo) are the B operands of S^T = K Q^T
   // and dP^T = V dO^T
@@ -483,11 +461,8 @@ void attn_bwd_dq_kernel(
   // bias (0, or -inf for a redundant key or one past the range) of key
   // block kb, written into its slot by wavefront 0
   auto write_bias = [&](int kb) {
-    if (w == 0 && lane < kQBK && kb < nkb) {
-      const int64_t kk = (int64_t)kb * kQBK + lane;
-      const bool red = kk >= kend || ((fl_bits[kk >> 6] >> (kk & 63)) & 1u);
-      slot(kb)->bias[lane] = red ? -INFINITY : 0.f;
-    }
+    if (w == 0 && lane < kQBK && kb < nkb)
+      slot(kb)->bias[lane] = key_bias(fl_bits, (int64_t)kb * kQBK + lane, kend);
   };
   // Iteration kb (-1 .. nkb - 1) waits for block kb + 2, has wavefront 0
   // write block kb + 2's bias (read after the next barrier), and issues
@@ -700,7 +675,6 @@ void attn_bwd_dq_kernel(
   }
 }
 
-constexpr size_t kMaxLds = 160 * 1024;   // LDS of one CU
 
 lh_status launch_attn_bwd_dkv_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                    const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,

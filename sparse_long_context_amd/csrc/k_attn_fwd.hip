@@ -6,222 +6,201 @@
 // in the forward.
 //
 // Mask: query j sees keys j' <= j whose row is not REDUNDANT (a per-key -inf
-// bias staged in LDS next to each key tile).
+// bias staged in LDS next to each key block).
 //
 // Work decomposition.  A workgroup owns 128 queries of one (b, h) and has 8
-// wavefronts in two groups of 4; group g takes the key blocks of 64 with
-// index = g (mod 2), so two wavefronts share each SIMD and one's softmax
-// overlaps the other's MFMAs.  At the end group 1 hands its partial (max,
-// sum, output) to group 0 through LDS and group 0 merges them in a fixed
-// order.  The grid is one-dimensional, heaviest query blocks first over all
-// heads, so the dispatcher hands out work longest-first.
+// wavefronts in two groups of 4 (32 queries per wavefront, held in
+// registers as the B operand of S^T = K Q^T); group g takes the key blocks
+// of 32 with index = g (mod 2), so two wavefronts share each SIMD and one's
+// softmax overlaps the other's MFMAs.  Key-block pairs (K, V rows and each
+// key's bias) stream through an LDS ring of three pairs by direct
+// buffer->LDS loads, two pairs ahead, with LDS-side barriers and explicit
+// counts of the outstanding loads.  At the end group 1 hands its partial
+// (max, sum, output) to group 0 through LDS and group 0 merges them in a
+// fixed order.  The grid is one-dimensional, heaviest query blocks first
+// over all heads, so the dispatcher hands out work longest-first.
 //
-// Per wavefront (32 queries) and key block: S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16, the query being the MFMA column, so each lane
-// holds one query's logits (two lanes per query, one per half of the keys).
-// Those accumulator registers are the B operand of O^T += V^T P^T once P is
-// formed; both operands use the same key permutation inside each 16-key step.
-// P enters as a two-term bf16 split (hi + lo), so its rounding stays near
-// 2^-17 relative even where V carries large values.  The reference maximum
-// is only moved (and O, l rescaled) when a row's maximum grows by more than
-// 2^8, which keeps P <= 256.
-//
-// Tiles reach LDS by direct buffer->LDS loads (buffer_load_dwordx4 ... lds),
-// double-buffered, in an XOR-swizzled layout (no padding) that keeps the
-// MFMA operand reads free of bank conflicts.
+// Per wavefront and key block: S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+// (lane: one query, the 16 keys 8I + 4h + J of its half), an online softmax
+// whose reference maximum only moves (and O, l are rescaled) when a query's
+// maximum grows by more than 2^8, which keeps P <= 256, and O^T += V^T P^T
+// with V^T read from the V rows by the transposing LDS read and P entering
+// as a two-term bf16 split (hi + lo), so its rounding stays near 2^-17
+// relative even where V carries large values.
 #include "lh_mfma.h"
 
 namespace lh {
 
-constexpr int kFwdBM = 128;   // queries per workgroup
-constexpr int kFwdBN = 64;    // keys per block
-constexpr int kFwdThreads = 512;
+constexpr int kFwdBQ = 128;        // queries per workgroup (32 per wavefront)
+constexpr int kFwdThreads = 512;   // two groups of 4 wavefronts
+constexpr int kFwdPairs = 3;       // LDS ring of key-block pairs
 
 template <int D>
-struct FwdSmem {
-  bf16_t k[2][2][kFwdBN * D];   // [group][buffer] key rows, swizzled 16-byte chunks
-  bf16_t vt[2][2][D * kFwdBN];  // [group][buffer] V^T rows (head dim), swizzled
-  float bias[2][2][kFwdBN];     // [group][buffer] 0 or -inf per key
-};
-
-// swizzle of 16-byte chunk positions inside a K row (D/8 chunks per row) and
-// inside a V^T row (8 chunks of keys per row)
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  return (r / (128 / D)) % (D / 8);
-}
-__device__ __forceinline__ int swz_v(int dd) { return (dd >> 1) & 7; }
-
-template <int D>
-__global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
-    const bf16_t *__restrict__ qs, const bf16_t *__restrict__ ks,
-    const bf16_t *__restrict__ vst, const uint8_t *__restrict__ flags, float *__restrict__ os,
-    float *__restrict__ lse, int64_t S, int64_t Sp, int32_t BH, float scale_log2) {
+__global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
+    const bf16_t *__restrict__ qs, const bf16_t *__restrict__ ks, const bf16_t *__restrict__ vs,
+    const uint8_t *__restrict__ flags, float *__restrict__ os, float *__restrict__ lse, int64_t S,
+    int32_t BH, float sl2) {
+  static_assert(kFwdPairs == 3, "pair i + 2 is issued into the slots of pair i - 1");
   extern __shared__ __align__(16) unsigned char smraw[];
-  FwdSmem<D> &sm = *reinterpret_cast<FwdSmem<D> *>(smraw);
-  constexpr int KSTEPS = D / 16;          // k-steps of QK^T
-  constexpr int DB = D / 32;              // 32-row blocks of O^T
-  constexpr int KLOADS = kFwdBN * D / 8 / 64 / 4;   // 1 KB loads per wavefront, K tile
-  constexpr int VLOADS = D * kFwdBN / 8 / 64 / 4;   // same for the V^T tile
+  KeyStage<D> *stg = reinterpret_cast<KeyStage<D> *>(smraw);
+  // REDUNDANT bits of keys 0 .. kend-1, one 64-bit word per 64 keys
+  uint64_t *fl_bits =
+      reinterpret_cast<uint64_t *>(smraw + sizeof(KeyStage<D>) * 2 * kFwdPairs);
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  // the wavefronts that copy tiles: one 1 KB piece of each tile apiece
+  constexpr int LOADERS = kKeyBlock * D / 8 < kFwdThreads ? kKeyBlock * D / 8 : kFwdThreads;
+  using Map = TileMap<D, kKeyBlock, LOADERS>;
+  constexpr int LP = 4 * Map::NP;   // tile loads per loading wavefront per pair
 
-  const int nqb = (int)((S + kFwdBM - 1) / kFwdBM);
+  const int nqb = (int)((S + kFwdBQ - 1) / kFwdBQ);
   const int item = (int)blockIdx.x;
-  const int qb = nqb - 1 - item / BH;     // heaviest first
+  const int qb = nqb - 1 - item / BH;             // heaviest first
   const int64_t bh = item % BH;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar
   const int grp = wave >> 2, wg = wave & 3, gtid = tid & 255;
   const int col = lane & 31, h = lane >> 5;
-  const int64_t q0w = (int64_t)qb * kFwdBM + wg * 32;
+  const int64_t q0w = (int64_t)qb * kFwdBQ + wg * 32;
   const int64_t q = q0w + col;
+  const brsrc Kg = make_rsrc(ks + bh * S * D, (uint32_t)(S * D * 2)),
+              Vg = make_rsrc(vs + bh * S * D, (uint32_t)(S * D * 2));
 
-  const bf16_t *Q = qs + bh * S * D;
-  const brsrc Kg = make_rsrc(ks + bh * S * D, (uint32_t)(S * D * 2));
-  const brsrc Vt = make_rsrc(vst + bh * (int64_t)D * Sp, (uint32_t)(D * Sp * 2));
-  const uint8_t *fl = flags + bh * S;
+  const int64_t kend = min(S, (int64_t)(qb + 1) * kFwdBQ);
+  const int nkb = (int)((kend + kKeyBlock - 1) / kKeyBlock);
+  const int npair = (nkb + 1) / 2;
+  stage_flag_bits<kFwdThreads>(fl_bits, flags + bh * S, kend, wave, lane);
 
+  // this lane's query: the B operand of S^T = K Q^T
   bf16x8 qreg[KSTEPS];
   {
-    const int64_t qc = min(q, S - 1);     // rows past S are never stored
+    const int64_t qc = (bh * S + min(q, S - 1)) * D + 8 * h;   // rows past S are never stored
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qreg[s] = ld_bf16x8(Q + qc * D + s * 16 + 8 * h);
+    for (int s = 0; s < KSTEPS; ++s) qreg[s] = ld_bf16x8(qs + qc + s * 16);
   }
+  // a wait the compiler sees: the register loads above are complete before
+  // the loop (otherwise it re-waits for them inside every iteration)
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-  const int64_t kend = min(S, (int64_t)(qb + 1) * kFwdBM);
-  const int nkb = (int)((kend + kFwdBN - 1) / kFwdBN);
-  const int niter = (nkb + 1) / 2;
+  Map map;
+  map.init(tid);
+  // stage of block g of pair p
+  auto stage = [&](int p, int g) { return &stg[(p % kFwdPairs) * 2 + g]; };
+  // both blocks of pair p (a block past the range reads rows it never uses,
+  // or zeros past S), so that every pair is the same number of loads
+  auto issue = [&](int p) {
+    if (p < npair && tid < LOADERS) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int64_t r0 = (int64_t)(2 * p + g) * kKeyBlock;
+        map.load(stage(p, g)->k, Kg, r0);
+        map.load(stage(p, g)->v, Vg, r0);
+      }
+    }
+  };
+  // the 64 keys of pair p: their bias, written by wavefront 0
+  auto write_bias = [&](int p) {
+    if (wave == 0 && p < npair)
+      stage(p, lane >> 5)->bias[lane & 31] =
+          key_bias(fl_bits, (int64_t)p * 2 * kKeyBlock + lane, kend);
+  };
+  // Iteration i (0 .. npair - 1) waits for pair i, has wavefront 0 write
+  // pair i + 1's bias (read after the next barrier), and issues pair i + 2
+  // into the slots of pair i - 1.
+  auto sync = [&](int i) {
+    if (i + 1 >= npair) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LP) : "memory");
+    lds_barrier();
+    write_bias(i + 1);
+    issue(i + 2);
+  };
 
-  // issue the async loads of key block kb into [grp][buf]
-#define LH_FWD_ISSUE(kb_, buf_)                                                               \
-  do {                                                                                        \
-    const int64_t k0_ = (int64_t)(kb_) * kFwdBN;                                              \
-    unsigned char *kdst = reinterpret_cast<unsigned char *>(sm.k[grp][buf_]);                 \
-    unsigned char *vdst = reinterpret_cast<unsigned char *>(sm.vt[grp][buf_]);                \
-    _Pragma("unroll") for (int i = 0; i < KLOADS; ++i) {                                     \
-      const int j = wg * KLOADS + i;               /* 1 KB piece of the tile */               \
-      const int chunk = j * 64 + lane;             /* 16-byte slot in LDS */                  \
-      const int r = chunk / (D / 8), p = chunk % (D / 8);                                     \
-      const int c = p ^ swz_k<D>(r);                                                          \
-      const int64_t key = min(k0_ + r, S - 1);     /* rows past S: -inf bias */               \
-      lds_dma<16>(Kg, kdst + j * 1024, (uint32_t)((key * D + c * 8) * 2));                    \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < VLOADS; ++i) {                                     \
-      const int j = wg * VLOADS + i;                                                          \
-      const int chunk = j * 64 + lane;                                                        \
-      const int dd = chunk / 8, p = chunk % 8;                                                \
-      const int c = p ^ swz_v(dd);                                                            \
-      lds_dma<16>(Vt, vdst + j * 1024, (uint32_t)(((int64_t)dd * Sp + k0_ + c * 8) * 2));      \
-    }                                                                                         \
-  } while (0)
-#define LH_FWD_BIAS(kb_)                                                                      \
-  ([&]() -> float {                                                                           \
-    const int64_t key_ = (int64_t)(kb_) * kFwdBN + (gtid & 63);                               \
-    return (key_ < S && !(fl[key_] & LH_ROW_REDUNDANT)) ? 0.f : -INFINITY;                    \
-  }())
-
-  f32x16 acc_o[DB];
+  f32x16 acc_o[DB];   // O^T: lane = query, rows = head-dim 8I + 4h + J of block b
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc_o[b] = zero16();
-  float m_ref = -INFINITY, l_half = 0.f;
+  float m_ref = -INFINITY;   // reference maximum (log2 units), equal in both halves
+  float l_half = 0.f;        // sum of P over this half's keys
 
-  if (grp < nkb) {
-    LH_FWD_ISSUE(grp, 0);
-    const float bv = LH_FWD_BIAS(grp);
-    if (gtid < kFwdBN) sm.bias[grp][0][gtid] = bv;
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int it = 0; it < niter; ++it) {
-    const int kb = 2 * it + grp, kbn = kb + 2, buf = it & 1;
-    float bnext = 0.f;
-    if (kbn < nkb) {
-      LH_FWD_ISSUE(kbn, buf ^ 1);
-      bnext = LH_FWD_BIAS(kbn);
-    }
-    const int64_t k0 = (int64_t)kb * kFwdBN;
-    if (kb < nkb && k0 <= q0w + 31) {   // wavefront-uniform
-      const bf16_t *kt = sm.k[grp][buf];
-      const bf16_t *vt = sm.vt[grp][buf];
-      const float *bias = sm.bias[grp][buf];
-      f32x16 acc_s[2];
+  // one key block: S^T, masks, online softmax, O^T += V^T P^T.  One code
+  // path for every block: the causal bound qmax is the query's index within
+  // the block on the diagonal and beyond the block elsewhere.
+  auto block = [&](const KeyStage<D> *__restrict__ sb, int qmax) {
+    bf16x8 a0[DB];   // first-step V^T operands, read ahead of the S MFMAs
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        acc_s[kk] = zero16();
-        const int r = kk * 32 + col;
+    for (int b = 0; b < DB; ++b) a0[b] = ld_colop<D>(sb->v, 0, 32 * b, lane);
+    f32x16 sa = zero16();
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const int c = (2 * s + h) ^ swz_k<D>(r);
-          const bf16x8 a = ld_bf16x8(kt + (r * (D / 8) + c) * 8);
-          acc_s[kk] = mfma32(a, qreg[s], acc_s[kk]);
-        }
-      }
-      // scaled logits (log2 units) with masks; row maximum
-      const bool diag = k0 + kFwdBN - 1 > q0w;
-      float mloc = -INFINITY;
+    for (int s = 0; s < KSTEPS; ++s) sa = mfma32(ld_rowop<D>(sb->k, col, s, h), qreg[s], sa);
+    float mloc = -INFINITY;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+    for (int I = 0; I < 4; ++I) {
+      const f32x4 bj = *reinterpret_cast<const f32x4 *>(sb->bias + 8 * I + 4 * h);
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          const int kl = kk * 32 + 8 * I + 4 * h;
-          const float4 bv = *reinterpret_cast<const float4 *>(bias + kl);
-          const float bj[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-          for (int J = 0; J < 4; ++J) {
-            float x = fmaf(acc_s[kk][4 * I + J], scale_log2, bj[J]);
-            if (diag && k0 + kl + J > q) x = -INFINITY;
-            acc_s[kk][4 * I + J] = x;
-            mloc = fmaxf(mloc, x);
-          }
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      // move the reference maximum only when the row maximum grew by > 2^8
-      const bool grow = mloc > m_ref + 8.f;
-      if (__any(grow)) {
-        const float m_new = grow ? mloc : m_ref;
-        const float alpha =
-            grow ? (m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new)) : 1.f;
-        m_ref = m_new;
-        l_half *= alpha;
-#pragma unroll
-        for (int b = 0; b < DB; ++b)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc_o[b][v] *= alpha;
-      }
-      const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-      float rs = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float pv = __builtin_amdgcn_exp2f(acc_s[kk][v] - mu);
-          acc_s[kk][v] = pv;
-          rs += pv;
-        }
-      l_half += rs;
-      // O^T += V^T P^T over four 16-key steps
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 phi, plo;
-        pack_split(acc_s[s >> 1], 8 * (s & 1), phi, plo);
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const int dd = b * 32 + col;
-          const bf16_t *row = vt + dd * kFwdBN;
-          const int c0 = (2 * s) ^ swz_v(dd), c1 = (2 * s + 1) ^ swz_v(dd);
-          const bf16x8 a = ld_bf16x4x2(row + c0 * 8 + 4 * h, row + c1 * 8 + 4 * h);
-          acc_o[b] = mfma32(a, phi, acc_o[b]);
-          acc_o[b] = mfma32(a, plo, acc_o[b]);
-        }
+      for (int J = 0; J < 4; ++J) {
+        const int v = 4 * I + J;
+        float x = fmaf(sa[v], sl2, bj[J]);
+        x = 8 * I + 4 * h + J > qmax ? -INFINITY : x;
+        sa[v] = x;
+        mloc = fmaxf(mloc, x);
       }
     }
-    if (kbn < nkb && gtid < kFwdBN) sm.bias[grp][buf ^ 1][gtid] = bnext;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-#undef LH_FWD_ISSUE
-#undef LH_FWD_BIAS
+    mloc = fmaxf(mloc, swap_halves(mloc));
+    // move the reference maximum only when the maximum grew by > 2^8
+    const bool grow = mloc > m_ref + 8.f;
+    if (__any(grow)) {
+      const float m_new = grow ? mloc : m_ref;
+      const float alpha =
+          grow ? (m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new)) : 1.f;
+      m_ref = m_new;
+      l_half *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_o[b][v] *= alpha;
+    }
+    const float mu = m_ref == -INFINITY ? 0.f : m_ref;
+    float rs = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = __builtin_amdgcn_exp2f(sa[v] - mu);
+      sa[v] = p;
+      rs += p;
+    }
+    l_half += rs;
+    // O^T += V^T P^T over two 16-key steps
+    bf16x8 phi, plo;
+    pack_split(sa, 0, phi, plo);
+    bf16x8 a1[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) a1[b] = ld_colop<D>(sb->v, 1, 32 * b, lane);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      acc_o[b] = mfma32(a0[b], phi, acc_o[b]);
+      acc_o[b] = mfma32(a0[b], plo, acc_o[b]);
+    }
+    pack_split(sa, 8, phi, plo);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      acc_o[b] = mfma32(a1[b], phi, acc_o[b]);
+      acc_o[b] = mfma32(a1[b], plo, acc_o[b]);
+    }
+  };
 
-  // merge: group 1 -> LDS -> group 0 (the tile buffers are free now)
+  // last key block of this wavefront (its diagonal, or the last one of S)
+  const int lw = q0w < S ? (int)min((int64_t)nkb - 1, (q0w + 31) / kKeyBlock) : -1;
+  write_bias(0);   // keys 0..63: written and read by wavefront 0's own flag chunk
+  issue(0);
+  issue(1);
+  for (int i = 0; i < npair; ++i) {
+    sync(i);
+    const int kb = 2 * i + grp;
+    if (kb <= lw)
+      block(stage(i, grp), kb == lw ? (int)(q - (int64_t)kb * kKeyBlock) : kKeyBlock);
+  }
+
+  // merge: group 1 -> LDS -> group 0 (the ring is free once every
+  // wavefront is past the barrier)
+  lds_barrier();
   float *xo = reinterpret_cast<float *>(smraw);            // [DB*16][256 lanes]
   float *xm = xo + 256 * DB * 16, *xl = xm + 256;
   if (grp == 1) {
@@ -232,18 +211,19 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     xm[gtid] = m_ref;
     xl[gtid] = l_half;
   }
-  __syncthreads();
-  if (grp == 0) {
+  lds_barrier();
+  if (grp == 0 && lw >= 0) {
     const float m1 = xm[gtid], l1 = xl[gtid];
     const float m = fmaxf(m_ref, m1);
     const float mu = m == -INFINITY ? 0.f : m;
     const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mu);
     const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mu);
     const float lh = l_half * a0 + l1 * a1;
-    const float l_tot = lh + __shfl_xor(lh, 32);
+    const float l_tot = lh + swap_halves(lh);
     if (q < S) {
       const float inv = 1.f / l_tot;
       float *orow = os + (bh * S + q) * D;
+      // lane: query; rows are head-dim 8I + 4h + J
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -254,8 +234,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
             const int v = 4 * I + J;
             o4[J] = (acc_o[b][v] * a0 + xo[(b * 16 + v) * 256 + gtid] * a1) * inv;
           }
-          const int dd = b * 32 + 8 * I + 4 * h;
-          *reinterpret_cast<float4 *>(orow + dd) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+          *reinterpret_cast<float4 *>(orow + b * 32 + 8 * I + 4 * h) =
+              make_float4(o4[0], o4[1], o4[2], o4[3]);
         }
       if (h == 0) lse[bh * S + q] = mu * 0.69314718055994531f + logf(l_tot);
     }
@@ -263,24 +243,27 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
 }
 
 lh_status launch_attn_fwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
-                               const bf16_t *vst, const uint8_t *flags, float *os, float *lse,
+                               const bf16_t *vs, const uint8_t *flags, float *os, float *lse,
                                hipStream_t st) {
   if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
-  const unsigned items = cdiv(g.S, kFwdBM) * (unsigned)g.BH();
+  const unsigned items = cdiv(g.S, kFwdBQ) * (unsigned)g.BH();
   const float sl2 = g.scale * 1.4426950408889634f;
-  if (g.d == 128) {
-    const size_t shm = sizeof(FwdSmem<128>);
-    (void)hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel<128>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(items), dim3(kFwdThreads), shm, st, qs,
-                       ks, vst, flags, os, lse, g.S, g.Sp, (int32_t)g.BH(), sl2);
-  } else {
-    const size_t shm = sizeof(FwdSmem<64>);
-    (void)hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel<64>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(items), dim3(kFwdThreads), shm, st, qs,
-                       ks, vst, flags, os, lse, g.S, g.Sp, (int32_t)g.BH(), sl2);
-  }
+  // LDS: the ring, then one REDUNDANT bit per key of the widest key range
+  // (the merge reuses the ring: 256 lanes x (16 DB + 2) floats)
+  const size_t flb = (size_t)((g.S + 63) / 64 * 8);
+#define LH_FWD(D)                                                                             \
+  do {                                                                                        \
+    static_assert(sizeof(KeyStage<D>) * 2 * kFwdPairs >= 256 * (16 * (D / 32) + 2) * 4,       \
+                  "the merge fits in the ring");                                              \
+    const size_t shm = sizeof(KeyStage<D>) * 2 * kFwdPairs + flb;                             \
+    if (shm > kMaxLds) return LH_ERR_UNSUPPORTED;                                             \
+    (void)hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel<D>,                          \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);          \
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3(items), dim3(kFwdThreads), shm, st, qs,  \
+                       ks, vs, flags, os, lse, g.S, (int32_t)g.BH(), sl2);                    \
+  } while (0)
+  if (g.d == 128) LH_FWD(128); else LH_FWD(64);
+#undef LH_FWD
   return hip_status();
 }
 

@@ -145,10 +145,10 @@ lh_status launch_attn_bwd_f32(const Geo &g, const float *qs, const float *ks, co
                               const float *dos, float *drow_ws, float *dqs, float *dks,
                               float *dvs, hipStream_t st);
 
-// attention, bf16 I/O (MFMA).  vst: transposed V [BH, d, Sp].  dO enters the
-// backward as a two-term bf16 split (hi + lo).
+// attention, bf16 I/O (MFMA), on the gathered rows [BH, S, d].  dO enters
+// the backward as a two-term bf16 split (hi + lo).
 lh_status launch_attn_fwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
-                               const bf16_t *vst, const uint8_t *flags, float *os, float *lse,
+                               const bf16_t *vs, const uint8_t *flags, float *os, float *lse,
                                hipStream_t st);
 lh_status launch_attn_bwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,

@@ -237,4 +237,53 @@ struct TileMap {
   }
 };
 
+// ---------------------------------------------------------------- key rings
+// The dQ and forward kernels stream key blocks of 32 rows (K, V and each
+// key's mask bias) through an LDS ring; the REDUNDANT flags of a
+// workgroup's key range are kept as bits.
+constexpr int kKeyBlock = 32;
+constexpr size_t kMaxLds = 160 * 1024;   // LDS of one CU
+
+template <int D>
+struct KeyStage {
+  bf16_t k[kKeyBlock * D];   // K rows of the block
+  bf16_t v[kKeyBlock * D];   // V rows
+  float bias[kKeyBlock];     // 0, or -inf for a redundant key or one past the range
+};
+
+// REDUNDANT bits of keys 0 .. kend-1 of one (b, h) into `bits` (one 64-bit
+// word per 64 keys): each wavefront of the NTHR threads packs 64-key chunks
+// with a ballot, 16 flag loads in flight per lane.  Readers need a barrier.
+template <int NTHR>
+__device__ __forceinline__ void stage_flag_bits(uint64_t *bits, const uint8_t *flags,
+                                                int64_t kend, int w, int lane) {
+  constexpr int FPT = 16, WAVES = NTHR / 64;
+  const int64_t nch = (kend + 63) / 64;
+  for (int64_t c0 = 0; c0 < nch; c0 += (int64_t)FPT * WAVES) {
+    uint8_t v[FPT];
+#pragma unroll
+    for (int j = 0; j < FPT; ++j) {
+      const int64_t i = (c0 + (int64_t)j * WAVES + w) * 64 + lane;
+      v[j] = i < kend ? flags[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < FPT; ++j) {
+      const int64_t c = c0 + (int64_t)j * WAVES + w;   // uniform over the wavefront
+      const uint64_t m = __ballot((v[j] & LH_ROW_REDUNDANT) != 0);
+      if (c < nch && lane == 0) bits[c] = m;
+    }
+  }
+}
+
+// the bias of key kk from the staged bits (keys at or past kend are masked)
+__device__ __forceinline__ float key_bias(const uint64_t *bits, int64_t kk, int64_t kend) {
+  const bool red = kk >= kend || ((bits[kk >> 6] >> (kk & 63)) & 1u);
+  return red ? -INFINITY : 0.f;
+}
+
+// the values of lanes l and l ^ 32 exchanged (v_permlane32_swap)
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32);
+}
+
 }  // namespace lh

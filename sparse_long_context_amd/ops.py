@@ -162,11 +162,11 @@ def attn_bwd_prep(c: Ctx, dos, os_):
     return hi, lo, drow
 
 
-def attn_fwd_mfma(c: Ctx, qs, ks, vst, flags, os_=None, lse=None):
+def attn_fwd_mfma(c: Ctx, qs, ks, vs, flags, os_=None, lse=None):
     dev = qs.device
     os_ = c.empty(*_bh(c), c.S, c.d, dtype=torch.float32, device=dev) if os_ is None else os_
     lse = c.empty(*_bh(c), c.S, dtype=torch.float32, device=dev) if lse is None else lse
-    c.call("lh_attn_fwd_mfma", _ptr(qs), _ptr(ks), _ptr(vst), _ptr(flags), _ptr(os_), _ptr(lse),
+    c.call("lh_attn_fwd_mfma", _ptr(qs), _ptr(ks), _ptr(vs), _ptr(flags), _ptr(os_), _ptr(lse),
            _stream())
     return os_, lse
 
@@ -233,8 +233,6 @@ def alloc_saved(c: Ctx, device):
             s[n] = torch.empty(*bh, c.E - c.N, c.d, dtype=c.io, device=device)
     for n in ("qs", "ks", "vs"):
         s[n] = torch.empty(*bh, c.S, c.d, dtype=c.io, device=device)
-    if c.io == torch.bfloat16:
-        s["vst"] = torch.empty(*bh, c.d, c.Sp, dtype=c.io, device=device)
     return s
 
 

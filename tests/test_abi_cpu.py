@@ -91,6 +91,14 @@ def test_span_mode_workspace_holds_the_owner_map(lib):
     assert span.ws_layer_bwd >= hold.ws_layer_bwd + owner
 
 
+def test_forward_attention_needs_no_workspace(lib):
+    # the MFMA forward reads the gathered V rows directly (no transposed copy)
+    for io in (L.LH_F32, L.LH_BF16):
+        z = L.Sizes()
+        assert lib.lh_get_sizes(C.byref(dims(io_dtype=io, out_dtype=io)), C.byref(z)) == L.LH_OK
+        assert z.ws_attn_fwd == 0
+
+
 def test_sizes_c4_shape(lib):
     d = dims(N=131072, H=8, d=128, p=4, L=6, K=8064, S=8192, io_dtype=L.LH_BF16,
              out_dtype=L.LH_BF16)
@@ -129,7 +137,7 @@ def test_stage_calls_reject_bad_args_without_launch(lib):
     # missing workspace
     d2 = dims(io_dtype=L.LH_BF16, out_dtype=L.LH_BF16)
     p = P(0x10000)
-    assert lib.lh_subseq_attn_fwd(C.byref(d2), p, p, p, p, p, p, None, 0, None) == \
+    assert lib.lh_subseq_attn_bwd(C.byref(d2), *([p] * 10), None, 0, None) == \
         L.LH_ERR_WORKSPACE
     s = L.Saved(*([0x10000] * 17))
     assert lib.lh_layer_bwd(C.byref(d2), C.byref(s), p, p, p, p, None, 0, None) == \
