@@ -79,6 +79,14 @@ typedef int32_t lh_status;
                                 selected entry whose span holds t (acausal
                                 inside a span, causal across coarsest cells) */
 
+/* lh_dims.sigma_mode: how an entry's two scores combine into the one score
+ * the stratified top-K ranks (the pages give two scores per cell and leave
+ * their combination open).  Every mode keeps a parent's score at least its
+ * children's, since both planes are max-pooled and non-negative. */
+#define LH_SIGMA_SUM     0   /* float32(sq + sk), the default reading       */
+#define LH_SIGMA_MAX     1   /* max(sq, sk)                                 */
+#define LH_SIGMA_PRODUCT 2   /* float32(sq * sk)                            */
+
 typedef void *lh_stream;     /* a hipStream_t */
 
 /* Problem statement of one layer call (explainer section 2.A-2.C: sequence
@@ -88,7 +96,8 @@ typedef void *lh_stream;     /* a hipStream_t */
  *   K >= 0, K % n_c == 0, K / n_c <= T - 1, S == K + n_c,
  *   E < 2^31, d in {64, 128}, io_dtype/out_dtype in {LH_F32, LH_BF16},
  *   out_dtype == LH_F32 when io_dtype == LH_F32, scale >= 0 and finite,
- *   scatter_mode in {LH_SCATTER_HOLD, LH_SCATTER_SPAN}. */
+ *   scatter_mode in {LH_SCATTER_HOLD, LH_SCATTER_SPAN},
+ *   sigma_mode in {LH_SIGMA_SUM, LH_SIGMA_MAX, LH_SIGMA_PRODUCT}. */
 typedef struct lh_dims {
   int64_t B;
   int64_t N;
@@ -102,6 +111,7 @@ typedef struct lh_dims {
   int32_t out_dtype;  /* O, OS, dQ, dK, dV                                   */
   float scale;        /* softmax scale; 0 selects 1/sqrt(d)                  */
   int32_t scatter_mode; /* LH_SCATTER_HOLD (0) or LH_SCATTER_SPAN (1)        */
+  int32_t sigma_mode;   /* LH_SIGMA_SUM (0), LH_SIGMA_MAX (1), LH_SIGMA_PRODUCT */
 } lh_dims;
 
 /* Buffers the forward fills and the backward reads (all caller-owned).

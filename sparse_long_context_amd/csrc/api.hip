@@ -22,6 +22,9 @@ lh_status make_geo(const lh_dims *dm, Geo *g) {
     return LH_ERR_INVALID_ARG;
   if (dm->scatter_mode != LH_SCATTER_HOLD && dm->scatter_mode != LH_SCATTER_SPAN)
     return LH_ERR_INVALID_ARG;
+  if (dm->sigma_mode != LH_SIGMA_SUM && dm->sigma_mode != LH_SIGMA_MAX &&
+      dm->sigma_mode != LH_SIGMA_PRODUCT)
+    return LH_ERR_INVALID_ARG;
   if (dm->L >= kMaxLevels) return LH_ERR_UNSUPPORTED;
   if (!(dm->scale >= 0.0f) || !isfinite(dm->scale)) return LH_ERR_INVALID_ARG;
   if ((dm->io_dtype != LH_F32 && dm->io_dtype != LH_BF16) ||
@@ -31,6 +34,7 @@ lh_status make_geo(const lh_dims *dm, Geo *g) {
   g->B = dm->B; g->N = dm->N; g->H = dm->H; g->d = dm->d; g->p = dm->p; g->L = dm->L;
   g->K = dm->K; g->S = dm->S; g->io = dm->io_dtype; g->out = dm->out_dtype;
   g->mode = dm->scatter_mode;
+  g->sigma = dm->sigma_mode;
   g->pw[0] = 1;
   for (int l = 1; l <= g->L; ++l)
     if (!mul_ok(g->pw[l - 1], g->p, lim, &g->pw[l])) return LH_ERR_INVALID_ARG;

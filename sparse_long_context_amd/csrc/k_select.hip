@@ -10,7 +10,8 @@
 //
 // Readings (stated in the design notes): a stratum is one coarsest cell with
 // its subtree; its root is always kept and k_s = K/n_c further entries are
-// taken by sigma = float32(sq + sk) descending, ties to the lower flat index;
+// taken by sigma descending, ties to the lower flat index, with sigma =
+// float32(sq + sk) (or, by sigma_mode, max(sq, sk) or float32(sq * sk));
 // rows follow (anchor, level) ascending; an entry is REDUNDANT when all its
 // children are selected or redundant; a LEADER is the first row at its anchor.
 //
@@ -38,7 +39,7 @@ struct SelArgs {
   int32_t *sel_idx, *sel_anchor, *row_of;
   uint8_t *sel_flags;
   int64_t N, E, S, Bc, k_s;
-  int32_t p, L, T;
+  int32_t p, L, T, sigma;
   int64_t lsize[kMaxLevels], loff[kMaxLevels], pw[kMaxLevels + 1];
   int32_t cstart[kMaxLevels + 1];   // first candidate index of each level
   int32_t tsub[kMaxLevels];         // subtree size of a level-l entry
@@ -94,7 +95,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
     const int l = level_of_cand(a, ci);
     const int j = ci - a.cstart[l];
     const int64_t f = a.loff[l] + m * (a.Bc / a.pw[l]) + j;
-    const float sg = __fadd_rn(sq[f], sk[f]);
+    const float sg = a.sigma == LH_SIGMA_SUM   ? __fadd_rn(sq[f], sk[f])
+                     : a.sigma == LH_SIGMA_MAX ? fmaxf(sq[f], sk[f])
+                                               : __fmul_rn(sq[f], sk[f]);
     key[ci] = __float_as_uint(sg);
     st[ci] = 0;
     int post = a.tsub[l] - 1;
@@ -216,7 +219,7 @@ lh_status launch_select(const Geo &g, const float *sq, const float *sk, int32_t 
   a.sq = sq; a.sk = sk; a.sel_idx = sel_idx; a.sel_anchor = sel_anchor; a.row_of = row_of;
   a.sel_flags = sel_flags;
   a.N = g.N; a.E = g.E; a.S = g.S; a.Bc = g.Bc; a.k_s = g.k_s;
-  a.p = g.p; a.L = g.L; a.T = (int32_t)g.T;
+  a.p = g.p; a.L = g.L; a.T = (int32_t)g.T; a.sigma = g.sigma;
   for (int l = 0; l < kMaxLevels; ++l) { a.lsize[l] = g.lsize[l]; a.loff[l] = g.loff[l]; }
   for (int l = 0; l <= kMaxLevels; ++l) a.pw[l] = g.pw[l];
   int cs = 0;

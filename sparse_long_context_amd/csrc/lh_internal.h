@@ -20,6 +20,7 @@ struct Geo {
   int32_t H, d, p, L;
   int32_t io, out;
   int32_t mode;                  // LH_SCATTER_HOLD or LH_SCATTER_SPAN
+  int32_t sigma;                 // LH_SIGMA_SUM, LH_SIGMA_MAX or LH_SIGMA_PRODUCT
   float scale;                   // softmax scale (1/sqrt(d) when dims say 0)
   int64_t lsize[kMaxLevels];     // N / p^l
   int64_t loff[kMaxLevels];      // flat offset of level l

@@ -63,6 +63,10 @@ CASES = [
     Case("bf16-p3", 1080, 2, 64, 3, 4, 10, structure="spikes"),
     # a single coarsest cell: n_c = 1, S = 101 (less than one tile)
     Case("bf16-one-stratum", 1024, 2, 128, 4, 6, 100),
+    # the pages' ablation point p = 2, L = 3, k = 1536, in the one form the
+    # stratification admits: 1536 coarsest cells of 4 tokens, one ranked
+    # entry each (K = 1536, S = 3072)
+    Case("bf16-p2-L3-k1536", 6144, 2, 64, 2, 3, 1, structure="lognormal"),
 ]
 
 

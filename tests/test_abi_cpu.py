@@ -78,6 +78,15 @@ def test_validate_null_and_scatter_mode(lib):
         assert lib.lh_validate(C.byref(d)) == code, mode
 
 
+def test_validate_sigma_mode(lib):
+    d = dims()
+    for mode, code in ((L.LH_SIGMA_SUM, L.LH_OK), (L.LH_SIGMA_MAX, L.LH_OK),
+                       (L.LH_SIGMA_PRODUCT, L.LH_OK), (3, L.LH_ERR_INVALID_ARG),
+                       (-1, L.LH_ERR_INVALID_ARG)):
+        d.sigma_mode = mode
+        assert lib.lh_validate(C.byref(d)) == code, mode
+
+
 def test_span_mode_workspace_holds_the_owner_map(lib):
     d = dims(N=131072, H=8, d=128, p=4, L=6, K=8064, S=8192, io_dtype=L.LH_BF16,
              out_dtype=L.LH_BF16)
