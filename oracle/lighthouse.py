@@ -218,12 +218,24 @@ def scores(Q, K_, g: Geometry):
     return planes[0], planes[1]
 
 
-def sigma(sQ, sK):
+SIGMA_MODES = ("sum", "max", "product")
+
+
+def sigma(sQ, sK, mode="sum"):
     """R-5 (the pages are silent on how the two scores combine): one ranking
-    score per entry, sigma = float32(sQ + sK), added in float32."""
+    score per entry, sigma = float32(sQ + sK), added in float32.  The other
+    combinations, kept as options: the larger of the two, and their product
+    rounded once to float32.  Each keeps a parent's score at least its
+    children's (both planes are max-pooled and non-negative)."""
     sQ = np.asarray(sQ, dtype=np.float32)
     sK = np.asarray(sK, dtype=np.float32)
-    return (sQ + sK).astype(np.float32)
+    if mode == "sum":
+        return (sQ + sK).astype(np.float32)
+    if mode == "max":
+        return np.maximum(sQ, sK).astype(np.float32)
+    if mode == "product":
+        return (sQ * sK).astype(np.float32)
+    raise ValueError(mode)
 
 
 # --------------------------------------------------------------------------
@@ -534,17 +546,17 @@ class HeadForward:
 
 
 def head_forward(Q, K_, V, g: Geometry, scale=None, store=None, selection=None,
-                 scatter_mode="hold"):
+                 scatter_mode="hold", sigma_mode="sum"):
     """One head of the layer: pyramid -> scores -> selection -> gather ->
     attention -> scatter.  `selection` (a Selection) replaces the computed
     one, so downstream stages can be checked on a given selection.
     scatter_mode: "hold" (R-14, causal hold) or "span" (R-14', span
-    broadcast)."""
+    broadcast).  sigma_mode: how the two scores combine (R-5)."""
     g.check()
     d = np.asarray(Q).shape[1]
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     sQ, sK = scores(Q, K_, g)
-    sig = sigma(sQ, sK)
+    sig = sigma(sQ, sK, sigma_mode)
     sel = select(sig, g) if selection is None else selection
     Ql, Kl, Vl = (pyramid(X, g, store) for X in (Q, K_, V))
     QS, KS, VS = gather(Ql, sel.sel_idx), gather(Kl, sel.sel_idx), gather(Vl, sel.sel_idx)
@@ -575,11 +587,12 @@ def head_backward(fw: HeadForward, dO):
     return tuple(out) + (dOS, dQS, dKS, dVS)
 
 
-def layer_forward(Q, K_, V, p, L, K, scale=None, store=None, scatter_mode="hold"):
+def layer_forward(Q, K_, V, p, L, K, scale=None, store=None, scatter_mode="hold",
+                  sigma_mode="sum"):
     """[B, H, N, d] arrays -> list over (b, h) of HeadForward."""
     Q = np.asarray(Q)
     B, H, N, _ = Q.shape
     g = Geometry(N, p, L, K).check()
     return [[head_forward(Q[b, h], K_[b, h], V[b, h], g, scale, store,
-                          scatter_mode=scatter_mode)
+                          scatter_mode=scatter_mode, sigma_mode=sigma_mode)
              for h in range(H)] for b in range(B)]

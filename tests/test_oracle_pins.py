@@ -136,10 +136,39 @@ def test_scores_level0_is_l2_norm_and_coarse_is_span_max():
             assert sK[o + i] == sK[i * w:(i + 1) * w].max()
 
 
-def test_sigma_parent_dominates_children():
+def test_sigma_modes_closed_form():
+    # exact in float32; the sum and the product rank the first two entries
+    # in opposite orders
+    sQ = np.array([1.0, 2.0, 0.5, 3.0], np.float32)
+    sK = np.array([4.0, 2.5, 0.25, 0.0], np.float32)
+    assert list(orc.sigma(sQ, sK)) == [5.0, 4.5, 0.75, 3.0]
+    assert list(orc.sigma(sQ, sK, "max")) == [4.0, 2.5, 0.5, 3.0]
+    assert list(orc.sigma(sQ, sK, "product")) == [4.0, 5.0, 0.125, 0.0]
+    assert orc.sigma(sQ, sK, "product").dtype == np.float32
+    # one rounding of the exact product: 1 + 2^-12 squared needs 25 bits
+    a = np.float32(1 + 2.0 ** -12)
+    assert orc.sigma([a], [a], "product")[0] == np.float32(1 + 2.0 ** -11)
+    with pytest.raises(ValueError):
+        orc.sigma(sQ, sK, "min")
+
+
+@pytest.mark.parametrize("mode", orc.SIGMA_MODES)
+def test_sigma_reduces_to_one_plane(mode):
+    # max with a zero plane, product with a plane of ones and sum with a zero
+    # plane all rank by sQ alone: the selection equals the one made on sQ
+    g = orc.Geometry(1024, 4, 4, 16 * 10)
+    sQ, _ = orc.scores(rnd((1024, 8), 5), rnd((1024, 8), 6), g)
+    other = np.ones_like(sQ) if mode == "product" else np.zeros_like(sQ)
+    a = orc.select(orc.sigma(sQ, other, mode), g)
+    b = orc.select(np.asarray(sQ, np.float32), g)
+    assert np.array_equal(a.sel_idx, b.sel_idx) and np.array_equal(a.sel_flags, b.sel_flags)
+
+
+@pytest.mark.parametrize("mode", orc.SIGMA_MODES)
+def test_sigma_parent_dominates_children(mode):
     g = orc.Geometry(256, 4, 4, 0)
     sQ, sK = orc.scores(rnd((256, 8), 1), rnd((256, 8), 2), g)
-    s = orc.sigma(sQ, sK)
+    s = orc.sigma(sQ, sK, mode)
     for l in range(1, g.L):
         par = s[g.level_offsets[l]:g.level_offsets[l] + g.level_sizes[l]]
         ch = s[g.level_offsets[l - 1]:g.level_offsets[l - 1] + g.level_sizes[l - 1]].reshape(-1, 4)
