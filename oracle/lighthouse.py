@@ -587,6 +587,43 @@ def head_backward(fw: HeadForward, dO):
     return tuple(out) + (dOS, dQS, dKS, dVS)
 
 
+# --------------------------------------------------------------------------
+# R-19  lengths that are not a multiple of the coarsest span
+# --------------------------------------------------------------------------
+def padded_length(N, p, L):
+    """R-19 (the pages assume whole coarsest cells): a length N that is not
+    a multiple of B_c = p**(L-1) is extended to the next multiple."""
+    Bc = p ** (L - 1)
+    return -(-N // Bc) * Bc
+
+
+def _pad_rows(X, n):
+    X = np.asarray(X, dtype=np.float64)
+    return np.concatenate([X, np.zeros((n - X.shape[0], X.shape[1]))])
+
+
+def ragged_forward(Q, K_, V, p, L, K, **kw):
+    """R-19: one head on a sequence of any length N.  The sequence is
+    extended with zero rows (q = k = v = 0) to the next multiple of B_c,
+    the layer runs on the extended sequence (K counts ranked entries of the
+    extended geometry), and the outputs of the N real tokens are kept.
+    Causality keeps the real tokens' outputs free of the padding except
+    through the last stratum's selection.  Returns (HeadForward of the
+    extended sequence, O of the real tokens)."""
+    N = np.asarray(Q).shape[0]
+    Np = padded_length(N, p, L)
+    g = Geometry(Np, p, L, K).check()
+    fw = head_forward(_pad_rows(Q, Np), _pad_rows(K_, Np), _pad_rows(V, Np), g, **kw)
+    return fw, fw.O[:N]
+
+
+def ragged_backward(fw: HeadForward, dO):
+    """R-19: gradients of the real tokens: dO extended with zero rows."""
+    N = np.asarray(dO).shape[0]
+    dQ, dK, dV = head_backward(fw, _pad_rows(dO, fw.g.N))[:3]
+    return dQ[:N], dK[:N], dV[:N]
+
+
 def layer_forward(Q, K_, V, p, L, K, scale=None, store=None, scatter_mode="hold",
                   sigma_mode="sum"):
     """[B, H, N, d] arrays -> list over (b, h) of HeadForward."""

@@ -42,6 +42,33 @@ def test_finite_differences(mode):
                 assert abs(fd - grad[t, c]) < 1e-6 * (1 + abs(fd)), (which, t, c, fd, grad[t, c])
 
 
+@pytest.mark.parametrize("mode", ["hold", "span"])
+def test_finite_differences_ragged_length(mode):
+    # R-19: N = 27 with B_c = 4 runs on 28 tokens; the gradients of the 27
+    # real tokens against central differences of sum(O_real * dO)
+    N, p, L, d = 27, 2, 3, 3
+    Np = orc.padded_length(N, p, L)
+    K = 2 * (Np // 4)
+    Q, K_, V, dO = (rnd((N, d), s) for s in (11, 12, 13, 14))
+    fw, O = orc.ragged_forward(Q, K_, V, p, L, K, scatter_mode=mode)
+    grads = orc.ragged_backward(fw, dO)
+    h = 1e-6
+    X = [Q, K_, V]
+    for which, grad in enumerate(grads):
+        assert grad.shape == (N, d)
+        for t in range(N):
+            for c in range(d):
+                outs = []
+                for sgn in (1, -1):
+                    Xs = [x.copy() for x in X]
+                    Xs[which][t, c] += sgn * h
+                    f2, O2 = orc.ragged_forward(*Xs, p, L, K, scatter_mode=mode)
+                    assert np.array_equal(f2.sel.sel_idx, fw.sel.sel_idx)
+                    outs.append(np.sum(O2 * dO))
+                fd = (outs[0] - outs[1]) / (2 * h)
+                assert abs(fd - grad[t, c]) < 1e-6 * (1 + abs(fd)), (which, t, c, fd, grad[t, c])
+
+
 def torch_layer(Q, K, V, g, sel_idx, flags, scale):
     """Independent float64 torch forward for a fixed selection."""
     N, d = Q.shape

@@ -414,6 +414,55 @@ def test_block_causality_unconditional(mode):
         assert np.array_equal(pert.O[:b], base.O[:b])
 
 
+# ---------------------------------------------------------------- R-19 ragged lengths
+def test_padded_length():
+    assert orc.padded_length(257, 2, 5) == 272
+    assert orc.padded_length(256, 2, 5) == 256
+    assert orc.padded_length(1, 4, 3) == 16
+    assert orc.padded_length(1000, 4, 1) == 1000
+
+
+@pytest.mark.parametrize("mode", ["hold", "span"])
+@pytest.mark.parametrize("N,p,L,ks", [(257, 2, 5, 6), (1000, 4, 3, 5), (1090, 3, 4, 9)])
+def test_ragged_length_prefix(N, p, L, ks, mode):
+    # the strata before the last one are complete; causality and stratum-local
+    # selection make their tokens' outputs those of the layer run on those
+    # strata alone (the BF1-style partial-last-block gate at N = 257)
+    Bc = p ** (L - 1)
+    Np = orc.padded_length(N, p, L)
+    m = N // Bc
+    Q, K, V = rnd((N, 8), 21), rnd((N, 8), 22), rnd((N, 8), 23)
+    fw, O = orc.ragged_forward(Q, K, V, p, L, ks * (Np // Bc), scatter_mode=mode)
+    assert O.shape == (N, 8) and np.all(np.isfinite(O))
+    g = orc.Geometry(m * Bc, p, L, ks * m).check()
+    ref = orc.head_forward(Q[:m * Bc], K[:m * Bc], V[:m * Bc], g, scatter_mode=mode)
+    np.testing.assert_allclose(O[:m * Bc], ref.O, rtol=0, atol=1e-12)
+    r = m * (ks + 1)   # the rows of the complete strata (flat indices differ by geometry)
+    assert np.array_equal(fw.sel.sel_anchor[:r], ref.sel.sel_anchor)
+    assert np.array_equal(fw.sel.sel_level[:r], ref.sel.sel_level)
+    assert np.array_equal(fw.sel.sel_flags[:r], ref.sel.sel_flags)
+
+
+def test_ragged_length_pads_with_zero_rows():
+    # N = 1000, p = 4, L = 3: the last coarsest cell (tokens 992..1007) holds
+    # 8 real tokens, so its entry is their sum over 16, and the padded
+    # tokens score zero
+    N, p, L = 1000, 4, 3
+    X = rnd((N, 8), 31)
+    fw, _ = orc.ragged_forward(X, X, X, p, L, 0)
+    np.testing.assert_allclose(fw.Ql[2][-1], X[992:1000].sum(axis=0) / 16, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(fw.Ql[1][249], X[996:1000].mean(axis=0), rtol=0, atol=1e-15)
+    assert np.all(fw.Ql[1][250:] == 0) and np.all(fw.sQ[N:1008] == 0)
+
+
+def test_ragged_length_whole_cells_is_the_layer():
+    N, p, L, K = 256, 4, 3, 16 * 4
+    Q, K_, V = rnd((N, 8), 1), rnd((N, 8), 2), rnd((N, 8), 3)
+    fw, O = orc.ragged_forward(Q, K_, V, p, L, K)
+    ref = orc.head_forward(Q, K_, V, orc.Geometry(N, p, L, K))
+    assert np.array_equal(O, ref.O)
+
+
 # ---------------------------------------------------------------- adjoints
 def test_scatter_adjoint_dot_product():
     g, s, sel = _selection_case(1024, 4, 4, 13, 41, ties=True)
