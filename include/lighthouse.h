@@ -92,12 +92,19 @@ typedef void *lh_stream;     /* a hipStream_t */
 /* Problem statement of one layer call (explainer section 2.A-2.C: sequence
  * length N, pooling factor p, L levels, top-K budget K, subsequence length
  * S).  Constraints checked by lh_validate:
- *   B >= 1, H >= 1, N >= 1, p >= 2, L >= 1, N % p^(L-1) == 0,
+ *   B >= 1, H >= 1, N >= 1, p >= 2, L >= 1,
  *   K >= 0, K % n_c == 0, K / n_c <= T - 1, S == K + n_c,
  *   E < 2^31, d in {64, 128}, io_dtype/out_dtype in {LH_F32, LH_BF16},
  *   out_dtype == LH_F32 when io_dtype == LH_F32, scale >= 0 and finite,
  *   scatter_mode in {LH_SCATTER_HOLD, LH_SCATTER_SPAN},
- *   sigma_mode in {LH_SIGMA_SUM, LH_SIGMA_MAX, LH_SIGMA_PRODUCT}. */
+ *   sigma_mode in {LH_SIGMA_SUM, LH_SIGMA_MAX, LH_SIGMA_PRODUCT}.
+ * The geometry (levels, strata, E, n_c, ...) is that of N rounded up to
+ * whole coarsest cells of B_c = p^(L-1) tokens: n_c = ceil(N / B_c).  When N
+ * is not a multiple of B_c (the pages assume whole cells; the reading taken
+ * is zero padding), lh_layer_fwd / lh_layer_bwd extend q, k, v and dO with
+ * zero rows to n_c * B_c tokens in their workspace, run the layer on the
+ * extended sequence and return the outputs and gradients of the N real
+ * tokens; stage calls that take token tensors return LH_ERR_INVALID_ARG. */
 typedef struct lh_dims {
   int64_t B;
   int64_t N;
@@ -143,7 +150,8 @@ typedef struct lh_saved {
   float *lse;
 } lh_saved;
 
-/* Derived sizes of one call.  Byte counts cover all B*H heads. */
+/* Derived sizes of one call.  Byte counts cover all B*H heads; token
+ * tensors have the caller's N rows, everything else the padded geometry. */
 typedef struct lh_sizes {
   int64_t E, n_c, T, k_s, Bc, Sp;
   size_t pyramid_bytes;     /* one of pq/pk/pv        */
@@ -326,7 +334,8 @@ lh_status lh_gather_bwd(const lh_dims *dims, const float *dqs,
  * scatter (causal hold, or span broadcast per dims->scatter_mode).  Fills
  * every buffer of *saved and o [B,H,N,d] out_dtype.
  * Workspace: sizes.ws_layer_fwd bytes (may be 0 / NULL when that is 0; the
- * span owner map in span mode). */
+ * span owner map in span mode, the zero-padded q, k, v and o when N is not
+ * whole coarsest cells). */
 lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k,
                        const void *v, void *o, const lh_saved *saved,
                        void *ws, size_t ws_bytes, lh_stream stream);

@@ -39,7 +39,11 @@ lh_status make_geo(const lh_dims *dm, Geo *g) {
   for (int l = 1; l <= g->L; ++l)
     if (!mul_ok(g->pw[l - 1], g->p, lim, &g->pw[l])) return LH_ERR_INVALID_ARG;
   g->Bc = g->pw[g->L - 1];
-  if (g->Bc > g->N || g->N % g->Bc) return LH_ERR_INVALID_ARG;
+  // a length that is not whole coarsest cells: the layer calls run on the
+  // sequence extended with zero rows to the next multiple (stage calls that
+  // take token tensors need whole cells)
+  g->Nreal = dm->N;
+  g->N = (dm->N + g->Bc - 1) / g->Bc * g->Bc;
   g->n_c = g->N / g->Bc;
   g->T = (g->pw[g->L] - 1) / (g->p - 1);
   int64_t off = 0;
@@ -87,8 +91,15 @@ static size_t ws_attn_bwd(const Geo &g) {
   return 2 * al256(rows_bf16(g)) + al256(z.drow);        // dos split (hi, lo), drow
 }
 static size_t owner_bytes(const Geo &g) { return (size_t)g.BH() * g.N * 4; }
+static bool ragged(const Geo &g) { return g.N != g.Nreal; }
+// one padded token tensor [B,H,N,d] of element type t
+static size_t padded_bytes(const Geo &g, int32_t t) {
+  return (size_t)g.BH() * g.N * g.d * el_size(t);
+}
 static size_t ws_layer_fwd(const Geo &g) {
-  return g.mode == LH_SCATTER_SPAN ? al256(owner_bytes(g)) : 0;   // span owner map
+  size_t b = g.mode == LH_SCATTER_SPAN ? al256(owner_bytes(g)) : 0;   // span owner map
+  if (ragged(g)) b += 3 * al256(padded_bytes(g, g.io)) + al256(padded_bytes(g, g.out));
+  return b;
 }
 static size_t ws_layer_bwd(const Geo &g) {
   Sizes z = sizes_of(g);
@@ -96,8 +107,11 @@ static size_t ws_layer_bwd(const Geo &g) {
   if (g.io == LH_BF16) b += 2 * al256(rows_bf16(g));     // dos split
   else b += al256(z.subseq_f32);                          // float32 dos
   if (g.mode == LH_SCATTER_SPAN) b += al256(owner_bytes(g));
+  if (ragged(g)) b += 4 * al256(padded_bytes(g, g.out));  // dO, dQ, dK, dV padded
   return b;
 }
+// stage calls that read or write token tensors [B,H,N,d] need whole cells
+static lh_status need_whole(const Geo &g) { return ragged(g) ? LH_ERR_INVALID_ARG : LH_OK; }
 
 // carve consecutive 256-aligned sub-buffers out of a workspace
 struct Carver {
@@ -151,8 +165,8 @@ lh_status lh_get_sizes(const lh_dims *dims, lh_sizes *out) {
   if (g.io == LH_BF16 && bh * g.S * g.d * 2 > out->subseq_bytes) out->subseq_bytes = bh * g.S * g.d * 2;
   out->os_bytes = bh * g.S * g.d * 4;
   out->lse_bytes = bh * g.S * 4;
-  out->token_io_bytes = bh * g.N * g.d * el_size(g.io);
-  out->token_out_bytes = bh * g.N * g.d * el_size(g.out);
+  out->token_io_bytes = bh * g.Nreal * g.d * el_size(g.io);
+  out->token_out_bytes = bh * g.Nreal * g.d * el_size(g.out);
   out->ws_attn_fwd = ws_attn_fwd(g);
   out->ws_attn_bwd = ws_attn_bwd(g);
   out->ws_layer_fwd = ws_layer_fwd(g);
@@ -178,6 +192,7 @@ lh_status lh_pyramid_build(const lh_dims *dims, const void *q, const void *k, co
                            void *pq, void *pk, void *pv, lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
+  LH_TRY(need_whole(g));
   const void *in[3] = {q, k, v};
   void *out[3] = {pq, pk, pv};
   int any = 0;
@@ -194,6 +209,7 @@ lh_status lh_score(const lh_dims *dims, const void *q, const void *k, float *sq,
                    lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
+  LH_TRY(need_whole(g));
   LH_REQ(q && k && sq && sk && aligned16(q) && aligned16(k) && aligned4(sq) && aligned4(sk));
   return launch_pyramid_score(g, q, k, nullptr, nullptr, nullptr, nullptr, sq, sk,
                               (hipStream_t)stream);
@@ -204,6 +220,7 @@ lh_status lh_pyramid_score(const lh_dims *dims, const void *q, const void *k, co
                            lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
+  LH_TRY(need_whole(g));
   LH_REQ(q && k && v && sq && sk);
   LH_REQ(g.L == 1 || (pq && pk && pv));
   LH_REQ(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(pq) && aligned16(pk) &&
@@ -242,6 +259,7 @@ lh_status lh_gather(const lh_dims *dims, const void *q, const void *k, const voi
                     lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
+  LH_TRY(need_whole(g));
   LH_REQ(q && k && v && sel_idx && qs && ks && vs);
   LH_REQ(g.L == 1 || (pq && pk && pv));
   LH_REQ(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(pq) && aligned16(pk) &&
@@ -356,6 +374,7 @@ lh_status lh_scatter(const lh_dims *dims, const void *os, const int32_t *sel_anc
                      const uint8_t *sel_flags, void *o, lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
+  LH_TRY(need_whole(g));
   LH_REQ(os && sel_anchor && sel_flags && o);
   LH_REQ(aligned16(os) && aligned16(o) && aligned4(sel_anchor));
   return launch_scatter(g, (const float *)os, sel_anchor, sel_flags, o, (hipStream_t)stream);
@@ -365,6 +384,7 @@ lh_status lh_scatter_bwd(const lh_dims *dims, const void *dout, const int32_t *s
                          const uint8_t *sel_flags, float *dos, lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
+  LH_TRY(need_whole(g));
   LH_REQ(dout && sel_anchor && sel_flags && dos);
   LH_REQ(aligned16(dout) && aligned16(dos) && aligned4(sel_anchor));
   return launch_scatter_bwd(g, dout, sel_anchor, sel_flags, dos, nullptr, nullptr, nullptr,
@@ -375,6 +395,7 @@ lh_status lh_span_owner(const lh_dims *dims, const int32_t *row_of, int32_t *own
                         lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
+  LH_TRY(need_whole(g));
   LH_REQ(row_of && owner);
   LH_REQ(aligned4(row_of) && aligned4(owner));
   return launch_owner(g, row_of, owner, (hipStream_t)stream);
@@ -384,6 +405,7 @@ lh_status lh_scatter_span(const lh_dims *dims, const float *os, const int32_t *o
                           lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
+  LH_TRY(need_whole(g));
   LH_REQ(os && owner && o);
   LH_REQ(aligned16(os) && aligned4(owner) && aligned16(o));
   return launch_scatter_span(g, os, owner, o, (hipStream_t)stream);
@@ -394,6 +416,7 @@ lh_status lh_scatter_span_bwd(const lh_dims *dims, const void *dout, const int32
                               lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
+  LH_TRY(need_whole(g));
   LH_REQ(dout && sel_idx && sel_flags && owner && dos);
   LH_REQ(aligned16(dout) && aligned4(sel_idx) && aligned4(owner) && aligned16(dos));
   return launch_scatter_span_bwd(g, dout, sel_idx, sel_flags, owner, dos, nullptr, nullptr,
@@ -405,6 +428,7 @@ lh_status lh_gather_bwd(const lh_dims *dims, const float *dqs, const float *dks,
                         lh_stream stream) {
   Geo g;
   LH_TRY(make_geo(dims, &g));
+  LH_TRY(need_whole(g));
   LH_REQ(dqs && dks && dvs && row_of && dq && dk && dv);
   LH_REQ(aligned16(dqs) && aligned16(dks) && aligned16(dvs) && aligned4(row_of) &&
          aligned16(dq) && aligned16(dk) && aligned16(dv));
@@ -436,6 +460,24 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
   const size_t need = ws_layer_fwd(g);
   if (need && (ws_bytes < need || !ws || !aligned16(ws))) return LH_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
+  Carver c{(char *)ws, 0, ws_bytes};
+  int32_t *owner = g.mode == LH_SCATTER_SPAN ? (int32_t *)c.take(owner_bytes(g)) : nullptr;
+  void *o_run = o;
+  if (ragged(g)) {
+    // whole coarsest cells: the inputs extended with zero rows, the output
+    // written to a padded buffer and its real rows copied out at the end
+    const size_t tin = padded_bytes(g, g.io);
+    void *qp = c.take(tin), *kp = c.take(tin), *vp = c.take(tin);
+    o_run = c.take(padded_bytes(g, g.out));
+    const int64_t rb = (int64_t)g.d * el_size(g.io);
+    LH_TRY(launch_copy_rows(g, q, qp, g.Nreal, g.N, rb, st));
+    LH_TRY(launch_copy_rows(g, k, kp, g.Nreal, g.N, rb, st));
+    LH_TRY(launch_copy_rows(g, v, vp, g.Nreal, g.N, rb, st));
+    q = qp;
+    k = kp;
+    v = vp;
+  }
+  if (!c.ok()) return LH_ERR_WORKSPACE;
   LH_TRY(launch_pyramid_score(g, q, k, v, s->pq, s->pk, s->pv, s->sq, s->sk, st));
   LH_TRY(launch_select(g, s->sq, s->sk, s->sel_idx, s->sel_anchor, s->sel_flags, s->row_of, st));
   const bool bf = g.io == LH_BF16;
@@ -449,11 +491,14 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
     LH_TRY(launch_attn_fwd_f32(g, (const float *)s->qs, (const float *)s->ks,
                                (const float *)s->vs, s->sel_flags, (float *)s->os, s->lse, st));
   if (g.mode == LH_SCATTER_SPAN) {
-    int32_t *owner = (int32_t *)ws;
     LH_TRY(launch_owner(g, s->row_of, owner, st));
-    return launch_scatter_span(g, (const float *)s->os, owner, o, st);
+    LH_TRY(launch_scatter_span(g, (const float *)s->os, owner, o_run, st));
+  } else {
+    LH_TRY(launch_scatter(g, (const float *)s->os, s->sel_anchor, s->sel_flags, o_run, st));
   }
-  return launch_scatter(g, (const float *)s->os, s->sel_anchor, s->sel_flags, o, st);
+  if (ragged(g))
+    return launch_copy_rows(g, o_run, o, g.N, g.Nreal, (int64_t)g.d * el_size(g.out), st);
+  return LH_OK;
 }
 
 lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout, void *dq,
@@ -473,6 +518,17 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
   float *dvs = (float *)c.take(z.subseq_f32);
   float *drow = (float *)c.take(z.drow);
   int32_t *owner = g.mode == LH_SCATTER_SPAN ? (int32_t *)c.take(owner_bytes(g)) : nullptr;
+  void *grad[3] = {dq, dk, dv};
+  if (ragged(g)) {
+    // dO extended with zero rows; the gradients go to padded buffers whose
+    // real rows are copied out at the end
+    const size_t tout = padded_bytes(g, g.out);
+    void *dop = c.take(tout);
+    for (int i = 0; i < 3; ++i) grad[i] = c.take(tout);
+    if (!c.ok()) return LH_ERR_WORKSPACE;
+    LH_TRY(launch_copy_rows(g, dout, dop, g.Nreal, g.N, (int64_t)g.d * el_size(g.out), st));
+    dout = dop;
+  }
   // scatter adjoint in the layer's mode (dos float32 and/or its bf16 split)
   auto scatter_adj = [&](float *dos, bf16_t *hi, bf16_t *lo) -> lh_status {
     if (g.mode == LH_SCATTER_SPAN) {
@@ -500,8 +556,14 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
                                dos, drow, dqs, dks, dvs, st));
   }
   const float *in[3] = {dqs, dks, dvs};
-  void *out[3] = {dq, dk, dv};
-  return launch_unpool(g, in, s->row_of, out, st);
+  LH_TRY(launch_unpool(g, in, s->row_of, grad, st));
+  if (ragged(g)) {
+    void *out[3] = {dq, dk, dv};
+    for (int i = 0; i < 3; ++i)
+      LH_TRY(launch_copy_rows(g, grad[i], out[i], g.N, g.Nreal, (int64_t)g.d * el_size(g.out),
+                              st));
+  }
+  return LH_OK;
 }
 
 }  // extern "C"

@@ -332,6 +332,29 @@ lh_status launch_scatter_bwd(const Geo &g, const void *dout, const int32_t *sel_
   return hip_status();
 }
 
+// ---------------------------------------------------------------- row copies
+// Pads a [BH, rows_src, *] tensor with zero rows to rows_dst rows, or keeps
+// its first rows_dst rows; 16 bytes per thread.
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint4 *src, uint4 *dst,
+                                                        int64_t rows_src, int64_t rows_dst,
+                                                        int64_t row_vec) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // vector within the head
+  const int64_t bh = blockIdx.y;
+  if (i >= rows_dst * row_vec) return;
+  const int64_t r = i / row_vec;
+  dst[bh * rows_dst * row_vec + i] =
+      r < rows_src ? src[bh * rows_src * row_vec + i] : make_uint4(0u, 0u, 0u, 0u);
+}
+
+lh_status launch_copy_rows(const Geo &g, const void *src, void *dst, int64_t rows_src,
+                           int64_t rows_dst, int64_t row_bytes, hipStream_t st) {
+  const int64_t row_vec = row_bytes / 16;
+  dim3 grid(cdiv(rows_dst * row_vec, 256), (unsigned)g.BH());
+  hipLaunchKernelGGL(copy_rows_kernel, grid, dim3(256), 0, st, (const uint4 *)src, (uint4 *)dst,
+                     rows_src, rows_dst, row_vec);
+  return hip_status();
+}
+
 // ---------------------------------------------------------------- span broadcast
 // The other reading of the scatter-back: every token takes the output of the
 // finest selected entry whose span holds it (its owner); the stratum root is

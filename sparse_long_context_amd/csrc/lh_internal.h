@@ -19,6 +19,8 @@ struct Geo {
   int64_t B, N, K, S, E, n_c, T, k_s, Bc, Sp;
   int32_t H, d, p, L;
   int32_t io, out;
+  int64_t Nreal;                 // the caller's sequence length (N is it rounded up to
+                                 // whole coarsest cells: the layer pads with zero rows)
   int32_t mode;                  // LH_SCATTER_HOLD or LH_SCATTER_SPAN
   int32_t sigma;                 // LH_SIGMA_SUM, LH_SIGMA_MAX or LH_SIGMA_PRODUCT
   float scale;                   // softmax scale (1/sqrt(d) when dims say 0)
@@ -103,6 +105,10 @@ __device__ __forceinline__ void store8_split(bf16_t *hi, bf16_t *lo, const float
 
 // ---------------------------------------------------------------- launchers
 // Each returns LH_OK or LH_ERR_HIP / LH_ERR_UNSUPPORTED; none allocates.
+// rows of row_bytes bytes (a multiple of 16) per (b, h): dst row r takes src
+// row r for r < rows_src and zeros after it (pads or truncates a sequence)
+lh_status launch_copy_rows(const Geo &g, const void *src, void *dst, int64_t rows_src,
+                           int64_t rows_dst, int64_t row_bytes, hipStream_t st);
 lh_status launch_pyramid_score(const Geo &g, const void *q, const void *k, const void *v,
                                void *pq, void *pk, void *pv, float *sq, float *sk,
                                hipStream_t st);

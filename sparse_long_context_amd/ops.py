@@ -43,7 +43,7 @@ def make_dims(q: torch.Tensor, p: int, L_: int, S: int, out_dtype=None, scale: f
     """Dims of a call on q [B, H, N, d]; K is S minus the n_c kept roots."""
     B, H, N, d = q.shape
     Bc = p ** (L_ - 1)
-    n_c = N // Bc if Bc <= N else 0
+    n_c = -(-N // Bc)   # a partial last cell counts (the layer pads it with zero rows)
     io = LHDT[q.dtype]
     out = io if out_dtype is None else LHDT[out_dtype]
     return L.make_dims(B, N, H, d, p, L_, S - n_c, S, io, out, scale, SCATTER_MODES[scatter_mode],
@@ -59,6 +59,7 @@ class Ctx:
         L.check(st, "lh_validate")
         self.z = L.sizes(dims)
         self.B, self.H, self.N, self.d = dims.B, dims.H, dims.N, dims.d
+        self.Np = self.z.n_c * self.z.Bc   # N rounded up to whole coarsest cells
         self.S, self.E, self.Sp = dims.S, self.z.E, self.z.Sp
         self.io, self.out = TDT[dims.io_dtype], TDT[dims.out_dtype]
 
@@ -77,7 +78,7 @@ def pyramid_score(c: Ctx, q, k, v):
     dev = q.device
     for n, t in (("q", q), ("k", k), ("v", v)):
         _need(t, _bh(c) + (c.N, c.d), c.io, n)
-    pq, pk, pv = (c.empty(*_bh(c), c.E - c.N, c.d, dtype=c.io, device=dev) for _ in range(3))
+    pq, pk, pv = (c.empty(*_bh(c), c.E - c.Np, c.d, dtype=c.io, device=dev) for _ in range(3))
     sq, sk = (c.empty(*_bh(c), c.E, dtype=torch.float32, device=dev) for _ in range(2))
     c.call("lh_pyramid_score", _ptr(q), _ptr(k), _ptr(v), _ptr(pq), _ptr(pk), _ptr(pv),
            _ptr(sq), _ptr(sk), _stream())
@@ -89,7 +90,7 @@ def pyramid_build(c: Ctx, q=None, k=None, v=None):
     for n, t in (("q", q), ("k", k), ("v", v)):
         if t is not None:
             _need(t, _bh(c) + (c.N, c.d), c.io, n)
-            outs.append(c.empty(*_bh(c), c.E - c.N, c.d, dtype=c.io, device=t.device))
+            outs.append(c.empty(*_bh(c), c.E - c.Np, c.d, dtype=c.io, device=t.device))
         else:
             outs.append(None)
     c.call("lh_pyramid_build", _ptr(q), _ptr(k), _ptr(v), *(_ptr(o) for o in outs), _stream())
@@ -230,9 +231,9 @@ def alloc_saved(c: Ctx, device):
         "lse": torch.empty(*bh, c.S, dtype=torch.float32, device=device),
         "qst": None, "kst": None, "vst": None,
     }
-    if c.E > c.N:
+    if c.E > c.Np:
         for n in ("pq", "pk", "pv"):
-            s[n] = torch.empty(*bh, c.E - c.N, c.d, dtype=c.io, device=device)
+            s[n] = torch.empty(*bh, c.E - c.Np, c.d, dtype=c.io, device=device)
     for n in ("qs", "ks", "vs"):
         s[n] = torch.empty(*bh, c.S, c.d, dtype=c.io, device=device)
     return s

@@ -31,7 +31,7 @@ class Case:
 
     @property
     def n_c(self):
-        return self.N // self.p ** (self.L - 1)
+        return -(-self.N // self.p ** (self.L - 1))   # a partial last cell counts
 
     @property
     def S(self):

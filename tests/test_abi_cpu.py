@@ -47,7 +47,8 @@ def dims(**kw):
     ({}, L.LH_OK),
     (dict(io_dtype=L.LH_BF16, out_dtype=L.LH_BF16), L.LH_OK),
     (dict(io_dtype=L.LH_BF16, out_dtype=L.LH_F32), L.LH_OK),
-    (dict(N=4100), L.LH_ERR_INVALID_ARG),             # N % p^(L-1)
+    (dict(N=4100, K=257, S=514), L.LH_OK),            # N % p^(L-1): padded to 4112
+    (dict(N=4100), L.LH_ERR_INVALID_ARG),             # K % n_c with n_c = 257
     (dict(K=255, S=511), L.LH_ERR_INVALID_ARG),       # K % n_c
     (dict(K=256, S=513), L.LH_ERR_INVALID_ARG),       # S != K + n_c
     (dict(K=21 * 256, S=22 * 256), L.LH_ERR_INVALID_ARG),   # k_s > T-1
@@ -118,6 +119,22 @@ def test_sizes_c4_shape(lib):
     assert z.score_bytes == 8 * 174720 * 4
     assert z.token_io_bytes == 8 * 131072 * 128 * 2
     assert z.ws_layer_fwd == 0 and z.ws_layer_bwd > 4 * 8 * 8192 * 128 * 4
+
+
+def test_sizes_of_a_partial_last_cell(lib):
+    # N = 4100 with B_c = 16: the geometry is that of 4112 tokens (257 cells);
+    # token tensors keep 4100 rows; the layer workspaces hold the padded
+    # copies (q, k, v, o forward; dO, dQ, dK, dV backward)
+    whole, rag = L.Sizes(), L.Sizes()
+    assert lib.lh_get_sizes(C.byref(dims(N=4112, K=257, S=514)), C.byref(whole)) == L.LH_OK
+    assert lib.lh_get_sizes(C.byref(dims(N=4100, K=257, S=514)), C.byref(rag)) == L.LH_OK
+    assert (rag.E, rag.n_c, rag.T, rag.k_s, rag.Sp) == (whole.E, whole.n_c, whole.T, whole.k_s,
+                                                       whole.Sp)
+    assert rag.pyramid_bytes == whole.pyramid_bytes and rag.row_of_bytes == whole.row_of_bytes
+    assert rag.token_io_bytes == 2 * 4100 * 64 * 4
+    padded = 2 * 4112 * 64 * 4
+    assert rag.ws_layer_fwd == whole.ws_layer_fwd + 4 * padded
+    assert rag.ws_layer_bwd == whole.ws_layer_bwd + 4 * padded
 
 
 def test_ragged_sp(lib):

@@ -11,8 +11,8 @@ import pytest
 import torch
 
 from oracle import lighthouse as orc
-from tests.gpu_cases import (CASES, bh_pairs, f64, geometry, inputs, selection_from_gpu, store_of,
-                             tol_for)
+from tests.gpu_cases import (CASES, Case, bh_pairs, f64, geometry, inputs, selection_from_gpu,
+                             store_of, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -322,5 +322,42 @@ def test_layer_product_sigma_vs_oracle(case, dev):
         assert np.array_equal(saved["sel_idx"][b, h].cpu().numpy(), fw.sel.sel_idx)
         _close(f64(o[b, h]), fw.O, tol_for(case, fw.O, case.out), f"{case.name} h{h} O")
         gq, gk, gv = orc.head_backward(fw, f64(dOc[b, h]))[:3]
+        for got, want, n in ((dq, gq, "dQ"), (dk, gk, "dK"), (dv, gv, "dV")):
+            _close(f64(got[b, h]), want, tol_for(case, want, case.out), f"{case.name} h{h} {n}")
+
+
+# Lengths that are not whole coarsest cells (reading R-19): the layer pads
+# with zero rows in its workspace and returns the real tokens' outputs.
+RAGGED = [
+    # the partial-last-block gate length 257: 16 full cells of 16 and one token
+    Case("ragged-257", 257, 2, 64, 2, 5, 6),
+    # 62 full cells of 16 and a cell of 8 tokens, spiky rows, d = 128
+    Case("ragged-1000", 1000, 2, 128, 4, 3, 5, structure="spikes"),
+    # float32 I/O, one real token in the last cell
+    Case("ragged-f32-4001", 4001, 2, 64, 4, 3, 1, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("mode", ["hold", "span"])
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: c.name)
+def test_layer_ragged_length_vs_oracle(case, mode, dev):
+    Q, K, V, dO = (t.to(dev) for t in inputs(case))
+    c = _ctx(case, Q, scatter_mode=mode)
+    assert c.Np % case.p ** (case.L - 1) == 0 and c.Np > case.N
+    o, saved = ops.layer_fwd(c, Q, K, V)
+    dOc = dO.to(c.out)
+    dq, dk, dv = ops.layer_bwd(c, saved, dOc)
+    o2, saved2 = ops.layer_fwd(c, Q, K, V)
+    g2 = ops.layer_bwd(c, saved2, dOc)
+    torch.cuda.synchronize()
+    assert o.shape[2] == case.N and dq.shape[2] == case.N
+    assert torch.equal(o, o2) and all(torch.equal(a, b) for a, b in zip((dq, dk, dv), g2))
+    Kp = c.dims.K
+    for b, h in bh_pairs(case):
+        fw, O = orc.ragged_forward(f64(Q[b, h]), f64(K[b, h]), f64(V[b, h]), case.p, case.L, Kp,
+                                   store=store_of(case), scatter_mode=mode)
+        assert np.array_equal(saved["sel_idx"][b, h].cpu().numpy(), fw.sel.sel_idx)
+        _close(f64(o[b, h]), O, tol_for(case, O, case.out), f"{case.name} h{h} O")
+        gq, gk, gv = orc.ragged_backward(fw, f64(dOc[b, h]))
         for got, want, n in ((dq, gq, "dQ"), (dk, gk, "dK"), (dv, gv, "dV")):
             _close(f64(got[b, h]), want, tol_for(case, want, case.out), f"{case.name} h{h} {n}")
