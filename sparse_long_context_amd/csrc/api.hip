@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "lh_internal.h"
 
 namespace lh {
@@ -124,6 +126,35 @@ struct Carver {
   }
   bool ok() const { return off <= cap; }
 };
+
+// A second stream of each device (default priority, non-blocking) and two
+// events, created on first use and kept until the process ends: the layer
+// backward forks the pooling adjoint of dK and dV onto it so that it runs
+// beside the dQ kernel, and joins it back.  The mutex keeps each fork/join
+// sequence whole when several host threads call on one device.
+constexpr int kMaxDevices = 64;
+static std::mutex g_side_mu;
+static hipStream_t g_side[kMaxDevices];
+static hipEvent_t g_fork[kMaxDevices], g_join[kMaxDevices];
+static bool g_side_ok[kMaxDevices];
+
+// call with g_side_mu held
+static lh_status side_stream(hipStream_t *s, hipEvent_t *fork, hipEvent_t *join) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LH_ERR_HIP;
+  if (!g_side_ok[dev]) {
+    if (hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking) != hipSuccess)
+      return LH_ERR_HIP;
+    if (hipEventCreateWithFlags(&g_fork[dev], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&g_join[dev], hipEventDisableTiming) != hipSuccess)
+      return LH_ERR_HIP;
+    g_side_ok[dev] = true;
+  }
+  *s = g_side[dev];
+  *fork = g_fork[dev];
+  *join = g_join[dev];
+  return LH_OK;
+}
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 static bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
@@ -434,7 +465,7 @@ lh_status lh_gather_bwd(const lh_dims *dims, const float *dqs, const float *dks,
          aligned16(dq) && aligned16(dk) && aligned16(dv));
   const float *in[3] = {dqs, dks, dvs};
   void *out[3] = {dq, dk, dv};
-  return launch_unpool(g, in, row_of, out, (hipStream_t)stream);
+  return launch_unpool(g, in, row_of, out, 3, (hipStream_t)stream);
 }
 
 static lh_status check_saved(const Geo &g, const lh_saved *s) {
@@ -544,9 +575,28 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
     bf16_t *dlo = (bf16_t *)c.take(rows_bf16(g));
     if (!c.ok()) return LH_ERR_WORKSPACE;
     LH_TRY(scatter_adj(nullptr, dhi, dlo));
-    LH_TRY(launch_attn_bwd_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
-                                (const bf16_t *)s->vs, dhi, dlo, s->lse, drow, s->sel_flags, dqs,
-                                dks, dvs, st));
+    LH_TRY(launch_attn_bwd_dkv_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
+                                    (const bf16_t *)s->vs, dhi, dlo, s->lse, drow, s->sel_flags,
+                                    dks, dvs, st));
+    // dK, dV are final: their pooling adjoint runs on the side stream beside
+    // the dQ kernel (MFMA-bound; one wavefront per SIMD leaves room for it)
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    hipStream_t side;
+    hipEvent_t fork, join;
+    LH_TRY(side_stream(&side, &fork, &join));
+    if (hipEventRecord(fork, st) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess)
+      return LH_ERR_HIP;
+    const float *in_kv[2] = {dks, dvs};
+    void *out_kv[2] = {grad[1], grad[2]};
+    LH_TRY(launch_unpool(g, in_kv, s->row_of, out_kv, 2, side));
+    if (hipEventRecord(join, side) != hipSuccess) return LH_ERR_HIP;
+    LH_TRY(launch_attn_bwd_dq_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
+                                   (const bf16_t *)s->vs, dhi, dlo, s->lse, drow, s->sel_flags,
+                                   dqs, st));
+    const float *in_q[1] = {dqs};
+    void *out_q[1] = {grad[0]};
+    LH_TRY(launch_unpool(g, in_q, s->row_of, out_q, 1, st));
+    if (hipStreamWaitEvent(st, join, 0) != hipSuccess) return LH_ERR_HIP;
   } else {
     float *dos = (float *)c.take(z.subseq_f32);
     if (!c.ok()) return LH_ERR_WORKSPACE;
@@ -554,9 +604,9 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
     LH_TRY(launch_attn_bwd_f32(g, (const float *)s->qs, (const float *)s->ks,
                                (const float *)s->vs, (const float *)s->os, s->lse, s->sel_flags,
                                dos, drow, dqs, dks, dvs, st));
+    const float *in[3] = {dqs, dks, dvs};
+    LH_TRY(launch_unpool(g, in, s->row_of, grad, 3, st));
   }
-  const float *in[3] = {dqs, dks, dvs};
-  LH_TRY(launch_unpool(g, in, s->row_of, grad, st));
   if (ragged(g)) {
     void *out[3] = {dq, dk, dv};
     for (int i = 0; i < 3; ++i)

@@ -725,11 +725,15 @@ static int unpool_spw(const Geo &g) {
   return spw;
 }
 
-lh_status launch_unpool(const Geo &g, const float *const dxs[3], const int32_t *row_of,
-                        void *const dx[3], hipStream_t st) {
+lh_status launch_unpool(const Geo &g, const float *const dxs[], const int32_t *row_of,
+                        void *const dx[], int nt, hipStream_t st) {
   if (g.T > kUnpoolLdsEntries) return LH_ERR_UNSUPPORTED;
+  if (nt < 1 || nt > 3) return LH_ERR_INVALID_ARG;
   UnpoolArgs a;
-  for (int i = 0; i < 3; ++i) { a.dxs[i] = dxs[i]; a.dx[i] = dx[i]; }
+  for (int i = 0; i < 3; ++i) {
+    a.dxs[i] = i < nt ? dxs[i] : nullptr;
+    a.dx[i] = i < nt ? dx[i] : nullptr;
+  }
   a.row_of = row_of; a.N = g.N; a.E = g.E; a.S = g.S; a.Bc = g.Bc; a.d = g.d; a.L = g.L;
   a.p = g.p;
   a.spw = unpool_spw(g);
@@ -746,7 +750,7 @@ lh_status launch_unpool(const Geo &g, const float *const dxs[3], const int32_t *
     lb += a.spw * a.per[l];
   }
   const size_t smem = (size_t)a.spw * g.T * sizeof(int32_t);
-  dim3 grid((unsigned)(g.n_c / a.spw), (unsigned)g.BH(), 3);
+  dim3 grid((unsigned)(g.n_c / a.spw), (unsigned)g.BH(), (unsigned)nt);
   if (g.out == LH_BF16) {
     if (g.d == 128) hipLaunchKernelGGL((unpool_kernel<bf16_t, 16>), grid, dim3(kUnpoolThreads), smem, st, a);
     else hipLaunchKernelGGL((unpool_kernel<bf16_t, 8>), grid, dim3(kUnpoolThreads), smem, st, a);

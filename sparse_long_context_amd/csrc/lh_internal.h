@@ -141,8 +141,9 @@ lh_status launch_scatter_span_bwd(const Geo &g, const void *dout, const int32_t 
                                   const uint8_t *sel_flags, const int32_t *owner, float *dos,
                                   bf16_t *dos_hi, bf16_t *dos_lo, const float *os, float *drow,
                                   hipStream_t st);
-lh_status launch_unpool(const Geo &g, const float *const dxs[3], const int32_t *row_of,
-                        void *const dx[3], hipStream_t st);
+// the gather + pooling adjoints of nt (1..3) tensors: dxs[i] rows -> dx[i] tokens
+lh_status launch_unpool(const Geo &g, const float *const dxs[], const int32_t *row_of,
+                        void *const dx[], int nt, hipStream_t st);
 
 // attention, float32 I/O (VALU)
 lh_status launch_attn_fwd_f32(const Geo &g, const float *qs, const float *ks, const float *vs,
