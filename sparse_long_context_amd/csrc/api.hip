@@ -509,8 +509,23 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
     v = vp;
   }
   if (!c.ok()) return LH_ERR_WORKSPACE;
-  LH_TRY(launch_pyramid_score(g, q, k, v, s->pq, s->pk, s->pv, s->sq, s->sk, st));
-  LH_TRY(launch_select(g, s->sq, s->sk, s->sel_idx, s->sel_anchor, s->sel_flags, s->row_of, st));
+  // Q and K (pyramids and scores), then the V pyramid on the side stream
+  // beside the selection, which needs only the scores
+  LH_TRY(launch_pyramid_score(g, q, k, nullptr, s->pq, s->pk, nullptr, s->sq, s->sk, st));
+  {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    hipStream_t side;
+    hipEvent_t fork, join;
+    LH_TRY(side_stream(&side, &fork, &join));
+    if (hipEventRecord(fork, st) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess)
+      return LH_ERR_HIP;
+    LH_TRY(launch_pyramid_score(g, nullptr, nullptr, v, nullptr, nullptr, s->pv, nullptr, nullptr,
+                                side));
+    if (hipEventRecord(join, side) != hipSuccess) return LH_ERR_HIP;
+    LH_TRY(launch_select(g, s->sq, s->sk, s->sel_idx, s->sel_anchor, s->sel_flags, s->row_of,
+                         st));
+    if (hipStreamWaitEvent(st, join, 0) != hipSuccess) return LH_ERR_HIP;
+  }
   const bool bf = g.io == LH_BF16;
   LH_TRY(gather_impl(g, q, k, v, s->pq, s->pk, s->pv, s->sel_idx, s->qs, s->ks, s->vs, nullptr,
                      nullptr, nullptr, st));

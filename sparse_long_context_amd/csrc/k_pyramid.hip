@@ -43,6 +43,7 @@ struct PyrArgs {
   double rp[kMaxLevels];     // 1 / p^l
   double pwd[kMaxLevels];    // p^l
   int32_t pow2;              // p is a power of two: 1 / p^l is exact
+  int32_t zbase;             // tensor of blockIdx.z = 0 (tensors before it are skipped)
 };
 
 // float64 -> float32 rounding to odd: truncate toward zero and set the last
@@ -149,7 +150,7 @@ template <typename T, int CPR, int G>
 __global__ __launch_bounds__(kPyrThreads) void pyr_score_kernel(PyrArgs a) {
   extern __shared__ double lds[];                // [spw*R][d] sums, then [spw*R] maxima
   constexpr int U = 8;                           // token rows in flight per thread
-  const int z = blockIdx.z;
+  const int z = blockIdx.z + a.zbase;
   const T *X = (const T *)a.in[z];
   if (!X) return;
   const int64_t bh = blockIdx.y;
@@ -350,6 +351,9 @@ lh_status launch_pyramid_score(const Geo &g, const void *q, const void *k, const
   int nz = 0;
   for (int z = 0; z < 3; ++z) nz = a.in[z] ? z + 1 : nz;
   if (nz == 0) return LH_OK;
+  a.zbase = 0;
+  while (!a.in[a.zbase]) ++a.zbase;
+  nz -= a.zbase;
   const int cpr = g.d / 8;
   dim3 grid((unsigned)(g.n_c / a.spw), (unsigned)g.BH(), (unsigned)nz);
   dim3 block((unsigned)(a.spw * a.R * cpr));
