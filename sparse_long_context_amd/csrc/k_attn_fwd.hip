@@ -84,8 +84,10 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
 
   Map map;
   map.init(tid);
-  // stage of block g of pair p
-  auto stage = [&](int p, int g) { return &stg[(p % kFwdPairs) * 2 + g]; };
+  // stage of block g of pair p: each group's ring slots are contiguous, so
+  // that a slot fixed at compile time is an immediate offset (< 64 KB) from
+  // the group's base
+  auto stage = [&](int p, int g) { return &stg[g * kFwdPairs + p % kFwdPairs]; };
   // both blocks of pair p (a block past the range reads rows it never uses,
   // or zeros past S), so that every pair is the same number of loads
   auto issue = [&](int p) {
@@ -121,16 +123,20 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
   float m_ref = -INFINITY;   // reference maximum (log2 units), equal in both halves
   float l_half = 0.f;        // sum of P over this half's keys
 
-  // one key block: S^T, masks, online softmax, O^T += V^T P^T.  One code
-  // path for every block: the causal bound qmax is the query's index within
-  // the block on the diagonal and beyond the block elsewhere.
-  auto block = [&](const KeyStage<D> *__restrict__ sb, int qmax) {
-    bf16x8 a0[DB];   // first-step V^T operands, read ahead of the S MFMAs
+  // one key block: S^T, masks, online softmax, O^T += V^T P^T.  On the
+  // wavefront's diagonal block (a wave-uniform branch) keys past the query's
+  // index qmax within the block are masked as well.
+  auto block = [&](const KeyStage<D> *__restrict__ sb, bool diag, int qmax) {
+    // all K-row operands in flight at once, then the first-step V^T operands
+    bf16x8 kr[KSTEPS];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) kr[s] = ld_rowop<D>(sb->k, col, s, h);
+    bf16x8 a0[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) a0[b] = ld_colop<D>(sb->v, 0, 32 * b, lane);
     f32x16 sa = zero16();
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) sa = mfma32(ld_rowop<D>(sb->k, col, s, h), qreg[s], sa);
+    for (int s = 0; s < KSTEPS; ++s) sa = mfma32(kr[s], qreg[s], sa);
     float mloc = -INFINITY;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
@@ -138,12 +144,16 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         const int v = 4 * I + J;
-        float x = fmaf(sa[v], sl2, bj[J]);
-        x = 8 * I + 4 * h + J > qmax ? -INFINITY : x;
-        sa[v] = x;
-        mloc = fmaxf(mloc, x);
+        sa[v] = fmaf(sa[v], sl2, bj[J]);
       }
     }
+    if (diag) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (8 * (v >> 2) + 4 * h + (v & 3) > qmax) sa[v] = -INFINITY;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sa[v]);
     mloc = fmaxf(mloc, swap_halves(mloc));
     // move the reference maximum only when the maximum grew by > 2^8
     const bool grow = mloc > m_ref + 8.f;
@@ -191,11 +201,18 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
   write_bias(0);   // keys 0..63: written and read by wavefront 0's own flag chunk
   issue(0);
   issue(1);
-  for (int i = 0; i < npair; ++i) {
+  // pair i of this group's ring slot i % 3; unrolled by the ring size so
+  // that every slot is a constant offset from the group's base
+  const KeyStage<D> *mine = stg + grp * kFwdPairs;
+  auto step = [&](int i, const KeyStage<D> *sb) {
     sync(i);
     const int kb = 2 * i + grp;
-    if (kb <= lw)
-      block(stage(i, grp), kb == lw ? (int)(q - (int64_t)kb * kKeyBlock) : kKeyBlock);
+    if (kb <= lw) block(sb, kb == lw, (int)(q - (int64_t)kb * kKeyBlock));
+  };
+  for (int i = 0; i < npair; i += kFwdPairs) {
+    step(i, mine);
+    if (i + 1 < npair) step(i + 1, mine + 1);
+    if (i + 2 < npair) step(i + 2, mine + 2);
   }
 
   // merge: group 1 -> LDS -> group 0 (the ring is free once every
