@@ -9,19 +9,21 @@
 //
 // Two kernels, so that no sum needs atomics and results are bitwise
 // reproducible:
-//  * dK/dV: a workgroup owns 128 keys; its 8 wavefronts form two groups of
-//    4 (32 keys per wavefront) that take alternate 32-query blocks, from the
-//    diagonal to the end, and add their partial dK, dV in LDS at the end.
-//    S = Q K^T and dP = dO V^T have the key as the MFMA column, so the lanes
-//    holding P and dS are already the A operands of dV += P^T dO and
-//    dK += dS^T Q; the B operands dO and Q are read from the same row tiles
-//    with the LDS transposing read.  K sits in registers, V in LDS.
-//  * dQ: a workgroup owns 128 queries; two groups take alternate 32-key
-//    blocks up to the diagonal.  S^T = K Q^T and dP^T = V dO^T have the query
-//    as the column, and dS^T is the B operand of dQ^T += K^T dS^T, K^T again
-//    from the K row tile through the transposing read.
-// Row tiles arrive by direct global->LDS loads, double-buffered per group.
-// Grids are one-dimensional, heaviest blocks first over all heads.
+//  * dK/dV: a workgroup owns 128 keys and has 4 wavefronts, one per SIMD
+//    (32 keys each, up to 512 registers); every wavefront walks the 32-query
+//    blocks from its diagonal to the end.  S = Q K^T and dP = dO V^T have the
+//    key as the MFMA column, so the lanes holding P and dS are already the A
+//    operands of dV += P^T dO and dK += dS^T Q; the B operands dO and Q are
+//    read from the same row tiles with the LDS transposing read.  K and V of
+//    the wavefront's keys sit in registers.
+//  * dQ: a workgroup owns 128 queries (4 wavefronts, 32 queries each) and
+//    walks the 32-key blocks up to the diagonal.  S^T = K Q^T and
+//    dP^T = V dO^T have the query as the column, and dS^T is the B operand
+//    of dQ^T += K^T dS^T, K^T again from the K row tile through the
+//    transposing read.  Q and dO of the wavefront's queries sit in registers.
+// Row tiles arrive by direct buffer->LDS loads through a 5-slot ring, and
+// each kernel's loop is a three-block software pipeline (below).  Grids are
+// one-dimensional, heaviest blocks first over all heads.
 //
 // Products accumulate in float32.  dO, P and dS enter the MFMAs as two-term
 // bf16 splits (hi + lo; the lo*lo term is dropped), so their rounding stays
