@@ -129,9 +129,10 @@ struct Carver {
 
 // A second stream of each device (default priority, non-blocking) and two
 // events, created on first use and kept until the process ends: the layer
-// backward forks the pooling adjoint of dK and dV onto it so that it runs
-// beside the dQ kernel, and joins it back.  The mutex keeps each fork/join
-// sequence whole when several host threads call on one device.
+// forward forks the V pyramid onto it (beside the selection), the layer
+// backward the pooling adjoint of dK and dV (beside the dQ kernel), and each
+// joins it back.  The mutex keeps each fork/join sequence whole when several
+// host threads call on one device.
 constexpr int kMaxDevices = 64;
 static std::mutex g_side_mu;
 static hipStream_t g_side[kMaxDevices];
