@@ -530,17 +530,20 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
   const bool bf = g.io == LH_BF16;
   LH_TRY(gather_impl(g, q, k, v, s->pq, s->pk, s->pv, s->sel_idx, s->qs, s->ks, s->vs, nullptr,
                      nullptr, nullptr, st));
+  // bf16 I/O in hold mode: the attention kernel also writes the output
+  // under the causal hold (the scatter stage fused into its epilogue)
+  const bool fused = bf && g.mode != LH_SCATTER_SPAN;
   if (bf)
     LH_TRY(launch_attn_fwd_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
                                 (const bf16_t *)s->vs, s->sel_flags, (float *)s->os, s->lse,
-                                st));
+                                st, fused ? s->sel_anchor : nullptr, fused ? o_run : nullptr));
   else
     LH_TRY(launch_attn_fwd_f32(g, (const float *)s->qs, (const float *)s->ks,
                                (const float *)s->vs, s->sel_flags, (float *)s->os, s->lse, st));
   if (g.mode == LH_SCATTER_SPAN) {
     LH_TRY(launch_owner(g, s->row_of, owner, st));
     LH_TRY(launch_scatter_span(g, (const float *)s->os, owner, o_run, st));
-  } else {
+  } else if (!fused) {
     LH_TRY(launch_scatter(g, (const float *)s->os, s->sel_anchor, s->sel_flags, o_run, st));
   }
   if (ragged(g))

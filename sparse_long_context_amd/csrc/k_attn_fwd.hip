@@ -27,6 +27,8 @@
 // with V^T read from the V rows by the transposing LDS read and P entering
 // as a two-term bf16 split (hi + lo), so its rounding stays near 2^-17
 // relative even where V carries large values.
+#include <type_traits>
+
 #include "lh_mfma.h"
 
 namespace lh {
@@ -35,11 +37,111 @@ constexpr int kFwdBQ = 128;        // queries per workgroup (32 per wavefront)
 constexpr int kFwdThreads = 512;   // two groups of 4 wavefronts
 constexpr int kFwdPairs = 3;       // LDS ring of key-block pairs
 
-template <int D>
+// Layer output under the causal hold (the scatter stage, done by the
+// forward so that its writes overlap other workgroups' MFMA work): token t
+// takes the output row of the LEADER with the largest anchor <= t, and the
+// LEADER rows are exactly the rows whose anchor differs from the previous
+// row's.  This workgroup's leaders cover the token range [T0, T1): T0 is the
+// anchor of its first leader, T1 the end of its last leader's segment (the
+// next row with another anchor, possibly in the next workgroup); the
+// workgroup of row 0 also zero-fills the tokens before row 0's anchor.  The
+// output rows are staged in LDS as the output type (the same rounding as
+// the scatter stage), the token range is cut into one contiguous chunk per
+// group of lanes (one 16-byte piece of a token row per lane), and a group
+// walks its chunk with the row index, so each token is one LDS read and
+// one coalesced store.
+template <int D, int EPI>
+__device__ __forceinline__ void scatter_hold(unsigned char *smraw, int32_t *ep,
+                                             const f32x16 (&acc_o)[D / 32], int64_t R0,
+                                             int nrows, bool has_row, int wg, int col, int h,
+                                             int tid, int64_t bh, void *otok, int64_t N) {
+  using OT = typename std::conditional<EPI == 1, bf16_t, float>::type;
+  constexpr int DB = D / 32;
+  constexpr int RB = D * (int)sizeof(OT);   // bytes per output row
+  constexpr int CPT = RB / 16;              // lanes per token row
+  constexpr int NG = kFwdThreads / CPT;     // token groups
+  int32_t *ep_anc = ep, *ep_lead = ep + kFwdBQ;
+  lds_barrier();   // every wavefront is past the merge's LDS reads
+  unsigned char *orow = smraw;   // [kFwdBQ][RB]
+  if (has_row) {
+    const int r = wg * 32 + col;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int dd = b * 32 + 8 * I + 4 * h;
+        if constexpr (EPI == 1) {
+          *reinterpret_cast<uint2 *>(orow + r * RB + dd * 2) =
+              make_uint2(pack2_bf16(acc_o[b][4 * I], acc_o[b][4 * I + 1]),
+                         pack2_bf16(acc_o[b][4 * I + 2], acc_o[b][4 * I + 3]));
+        } else {
+          *reinterpret_cast<float4 *>(orow + r * RB + dd * 4) =
+              make_float4(acc_o[b][4 * I], acc_o[b][4 * I + 1], acc_o[b][4 * I + 2],
+                          acc_o[b][4 * I + 3]);
+        }
+      }
+  }
+  const int32_t a_prev = ep[2 * kFwdBQ + 1];
+  // the leader of each local row (-1: its leader is in the previous
+  // workgroup; such rows never hold the largest anchor <= t for t >= T0)
+  if (tid < nrows) {
+    int rr = tid;
+    while (rr > 0 && ep_anc[rr - 1] == ep_anc[tid]) --rr;
+    ep_lead[tid] = (rr == 0 && R0 > 0 && ep_anc[0] == a_prev) ? -1 : rr;
+  }
+  lds_barrier();
+  const int64_t T1 = ep[2 * kFwdBQ];
+  int r0 = 0;   // first local leader
+  while (r0 < nrows && ep_lead[r0] != r0) ++r0;
+  const int64_t T0 = r0 < nrows ? max((int64_t)0, min((int64_t)ep_anc[r0], N)) : T1;
+  const int64_t Z0 = R0 == 0 ? 0 : T0;   // row 0's workgroup: zeros before row 0's anchor
+  if (T1 <= Z0) return;
+  const int gi = tid / CPT, c = tid % CPT;
+  const int64_t chunk = (T1 - Z0 + NG - 1) / NG;
+  int64_t t = Z0 + gi * chunk;
+  const int64_t te = min(T1, t + chunk);
+  if (t >= te) return;
+  // last local row with anchor <= t (-1: none)
+  int lo = 0, hi = nrows;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)ep_anc[mid] <= t) lo = mid + 1; else hi = mid;
+  }
+  // r, the anchor of row r + 1 (the next boundary) and the source row's
+  // piece stay in registers: a token inside the current segment costs a
+  // compare and a store.  r < 0 only before row 0's anchor (zeros); for
+  // t >= T0 the row r is at or past the first leader, so its leader is local.
+  int r = lo - 1;
+  auto next_anchor = [&]() {
+    return r + 1 < nrows ? (int64_t)ep_anc[r + 1] : INT64_MAX;
+  };
+  auto piece = [&]() {
+    return r < 0 ? make_uint4(0, 0, 0, 0)
+                 : *reinterpret_cast<const uint4 *>(orow + ep_lead[r] * RB + c * 16);
+  };
+  int64_t nb = next_anchor();
+  uint4 val = piece();
+  unsigned char *dst = reinterpret_cast<unsigned char *>(otok) + bh * N * RB + c * 16;
+  for (; t < te; ++t) {
+    if (t >= nb) {
+      do {
+        ++r;
+        nb = next_anchor();
+      } while (t >= nb);
+      val = piece();
+    }
+    *reinterpret_cast<uint4 *>(dst + t * RB) = val;
+  }
+}
+
+// EPI: 0 = OS and lse only; 1 (bf16) or 2 (float32) = also the layer output
+// under the causal hold, written from this workgroup's rows (see the end).
+template <int D, int EPI>
 __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
     const bf16_t *__restrict__ qs, const bf16_t *__restrict__ ks, const bf16_t *__restrict__ vs,
     const uint8_t *__restrict__ flags, float *__restrict__ os, float *__restrict__ lse, int64_t S,
-    int32_t BH, float sl2) {
+    int32_t BH, float sl2, const int32_t *__restrict__ anchor, void *__restrict__ otok,
+    int64_t N) {
   static_assert(kFwdPairs == 3, "pair i + 2 is issued into the slots of pair i - 1");
   extern __shared__ __align__(16) unsigned char smraw[];
   KeyStage<D> *stg = reinterpret_cast<KeyStage<D> *>(smraw);
@@ -70,6 +172,27 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
   const int nkb = (int)((kend + kKeyBlock - 1) / kKeyBlock);
   const int npair = (nkb + 1) / 2;
   stage_flag_bits<kFwdThreads>(fl_bits, flags + bh * S, kend, wave, lane);
+  // output scatter: the anchors of this workgroup's rows (rows past S read
+  // as +inf), and the end of the last leader's segment (the anchor of the
+  // first later row with another anchor, or N) and the anchor of the row
+  // before the workgroup, for after the loop (the loop's barriers publish
+  // them)
+  const int64_t R0 = (int64_t)qb * kFwdBQ;
+  const int nrows = (int)min((int64_t)kFwdBQ, S - R0);
+  int32_t *ep = reinterpret_cast<int32_t *>(smraw + sizeof(KeyStage<D>) * 2 * kFwdPairs +
+                                            (S + 63) / 64 * 8);
+  if constexpr (EPI != 0) {
+    const int32_t *anc = anchor + bh * S;
+    if (tid < kFwdBQ) ep[tid] = tid < nrows ? anc[R0 + tid] : INT32_MAX;
+    if (tid == 0) {
+      const int32_t alast = anc[R0 + nrows - 1];
+      int64_t r = R0 + nrows;
+      while (r < S && anc[r] == alast) ++r;
+      const int64_t t1 = r < S ? (int64_t)anc[r] : N;
+      ep[2 * kFwdBQ] = (int32_t)max((int64_t)0, min(t1, N));
+      ep[2 * kFwdBQ + 1] = R0 > 0 ? anc[R0 - 1] : INT32_MIN;
+    }
+  }
 
   // this lane's query: the B operand of S^T = K Q^T
   bf16x8 qreg[KSTEPS];
@@ -250,6 +373,7 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
           for (int J = 0; J < 4; ++J) {
             const int v = 4 * I + J;
             o4[J] = (acc_o[b][v] * a0 + xo[(b * 16 + v) * 256 + gtid] * a1) * inv;
+            if constexpr (EPI != 0) acc_o[b][v] = o4[J];
           }
           *reinterpret_cast<float4 *>(orow + b * 32 + 8 * I + 4 * h) =
               make_float4(o4[0], o4[1], o4[2], o4[3]);
@@ -257,29 +381,42 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
       if (h == 0) lse[bh * S + q] = mu * 0.69314718055994531f + logf(l_tot);
     }
   }
+  if constexpr (EPI != 0) scatter_hold<D, EPI>(smraw, ep, acc_o, R0, nrows, grp == 0 && q < S,
+                                               wg, col, h, tid, bh, otok, N);
 }
 
 lh_status launch_attn_fwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                const bf16_t *vs, const uint8_t *flags, float *os, float *lse,
-                               hipStream_t st) {
+                               hipStream_t st, const int32_t *sel_anchor, void *o) {
   if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
   const unsigned items = cdiv(g.S, kFwdBQ) * (unsigned)g.BH();
   const float sl2 = g.scale * 1.4426950408889634f;
-  // LDS: the ring, then one REDUNDANT bit per key of the widest key range
-  // (the merge reuses the ring: 256 lanes x (16 DB + 2) floats)
+  // LDS: the ring, then one REDUNDANT bit per key of the widest key range,
+  // then (output scatter) the workgroup's anchors, leaders and two bounds.
+  // The merge reuses the ring (256 lanes x (16 DB + 2) floats), and so do
+  // the staged output rows.
   const size_t flb = (size_t)((g.S + 63) / 64 * 8);
-#define LH_FWD(D)                                                                             \
+  const int epi = o ? (g.out == LH_BF16 ? 1 : 2) : 0;
+  const size_t epb = o ? (2 * kFwdBQ + 2) * sizeof(int32_t) : 0;
+#define LH_FWD(D, E)                                                                          \
   do {                                                                                        \
     static_assert(sizeof(KeyStage<D>) * 2 * kFwdPairs >= 256 * (16 * (D / 32) + 2) * 4,       \
                   "the merge fits in the ring");                                              \
-    const size_t shm = sizeof(KeyStage<D>) * 2 * kFwdPairs + flb;                             \
+    static_assert(sizeof(KeyStage<D>) * 2 * kFwdPairs >= kFwdBQ * D * 4,                      \
+                  "the staged output rows fit in the ring");                                  \
+    const size_t shm = sizeof(KeyStage<D>) * 2 * kFwdPairs + flb + epb;                       \
     if (shm > kMaxLds) return LH_ERR_UNSUPPORTED;                                             \
-    (void)hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel<D>,                          \
+    (void)hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel<D, E>,                       \
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);          \
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3(items), dim3(kFwdThreads), shm, st, qs,  \
-                       ks, vs, flags, os, lse, g.S, (int32_t)g.BH(), sl2);                    \
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, E>), dim3(items), dim3(kFwdThreads), shm, st, \
+                       qs, ks, vs, flags, os, lse, g.S, (int32_t)g.BH(), sl2, sel_anchor, o,  \
+                       g.N);                                                                  \
   } while (0)
-  if (g.d == 128) LH_FWD(128); else LH_FWD(64);
+  if (g.d == 128) {
+    if (epi == 0) LH_FWD(128, 0); else if (epi == 1) LH_FWD(128, 1); else LH_FWD(128, 2);
+  } else {
+    if (epi == 0) LH_FWD(64, 0); else if (epi == 1) LH_FWD(64, 1); else LH_FWD(64, 2);
+  }
 #undef LH_FWD
   return hip_status();
 }

@@ -154,10 +154,13 @@ lh_status launch_attn_bwd_f32(const Geo &g, const float *qs, const float *ks, co
                               float *dvs, hipStream_t st);
 
 // attention, bf16 I/O (MFMA), on the gathered rows [BH, S, d].  dO enters
-// the backward as a two-term bf16 split (hi + lo).
+// the backward as a two-term bf16 split (hi + lo).  With `o` given, the
+// forward also writes the layer output o [BH, N, d] (out type) under the
+// causal hold from sel_anchor, as launch_scatter would.
 lh_status launch_attn_fwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                const bf16_t *vs, const uint8_t *flags, float *os, float *lse,
-                               hipStream_t st);
+                               hipStream_t st, const int32_t *sel_anchor = nullptr,
+                               void *o = nullptr);
 lh_status launch_attn_bwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
                                const float *lse, const float *drow, const uint8_t *flags,
