@@ -26,8 +26,13 @@ CFLAGS = [
 ]
 
 
+# per-file flags: the dQ kernel keeps MFMA results in VGPRs (its softmax
+# reads them there); the dK/dV kernel, with twice the accumulators, does not
+EXTRA = {"k_attn_bwd_dq.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, obj: str) -> tuple[str, int, str]:
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     return src, p.returncode, (p.stdout + p.stderr)
 

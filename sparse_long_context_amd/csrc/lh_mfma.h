@@ -141,6 +141,8 @@ __device__ __forceinline__ void lds_barrier() {
 // be moved below here by code motion (a scheduling fence alone does not stop
 // it).  Emits nothing.
 __device__ __forceinline__ void pin(const f32x16 &x) { asm volatile("" ::"a"(x)); }
+// the same, for a tile that stays in VGPRs
+__device__ __forceinline__ void pin_v(const f32x16 &x) { asm volatile("" ::"v"(x)); }
 
 // Issue-order prescriptions for the scheduler, within one fenced region:
 // NM times one MFMA followed by NR LDS reads (reads started early, under
