@@ -280,8 +280,12 @@ __global__ __launch_bounds__(256) void scatter_bwd_kernel(ScatBwdArgs a) {
     const int64_t t1 = max(t0, min(nx < a.S ? (int64_t)anc[nx] : a.N, a.N));
     const T *dO = (const T *)a.dout + bh * a.N * d + c * 8;
     // NF rows in flight per lane (raw, converted when added); each lane
-    // still adds its tokens in increasing order
-    constexpr int NF = sizeof(T) == 2 ? 16 : 8;
+    // still adds its tokens in increasing order.  Segments average ~21
+    // tokens, so 8 per lane (32 per wavefront) covers most in one batch and
+    // keeps the registers low enough for 7 wavefronts per SIMD: the kernel
+    // is bound by each wavefront's chain of dependent loads, so resident
+    // wavefronts count for more than depth
+    constexpr int NF = 8;
     for (int64_t t = t0 + u; t < t1; t += NF * TL) {
       Raw8<T> x[NF];
 #pragma unroll
