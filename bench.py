@@ -48,6 +48,8 @@ def parse():
                     help="skip the dense causal attention comparisons, torch SDPA and this "
                          "library's kernels at L=1 (a few seconds at the 128K workload)")
     ap.add_argument("--stage-reps", type=int, default=10)
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timings (L2 and Infinity Cache evicted before each rep)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known byte "
                          "count that calibrates hardware traffic counters)")
@@ -273,6 +275,31 @@ def main():
     value = w.B * w.N / (ms / 1e3)
     print(f"[bench] layer fwd+bwd {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # cold caches: before each rep a 1 GiB write evicts the L2 and the
+    # 256 MB Infinity Cache; events bracket the rep alone (the stream is in
+    # order, so the eviction has finished when the first event is reached)
+    evict = None if args.no_cold else torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def cold_ms(fn, reps):
+        tot = 0.0
+        for _ in range(reps):
+            evict.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            tot += a.elapsed_time(b)
+        return tot / reps
+
+    cold = None
+    if evict is not None:
+        cms = cold_ms(step, args.steps)
+        cold = {"ms_per_step": round(cms, 4), "tokens_per_s": round(w.B * w.N / (cms / 1e3), 1),
+                "how": "each step timed alone after a 1 GiB device write that evicts the L2 and the "
+                       "Infinity Cache; the headline value is the back-to-back (warm) rate"}
+        print(f"[bench] layer fwd+bwd cold {cms:.3f} ms/step", file=sys.stderr, flush=True)
+
     peaks = measured_peaks(torch, dev)
     print(f"[bench] measured ceilings {peaks}", file=sys.stderr, flush=True)
 
@@ -302,6 +329,11 @@ def main():
                 else:
                     ach = wk / (t / 1e3) / 1e9
                     ent.update({"gbs": round(ach, 1), "frac_hbm_peak": round(ach / HBM_PEAK_GBS, 4)})
+            if evict is not None:
+                tc = cold_ms(fn, args.stage_reps)
+                ent["ms_cold"] = round(tc, 4)
+                if wk is not None and name not in FLOP_STAGES:
+                    ent["gbs_cold"] = round(wk / (tc / 1e3) / 1e9, 1)
             stages[name] = ent
             return res
 
@@ -372,7 +404,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "N": w.N, "H": w.H, "d": w.d, "p": w.p,
                    "L": w.L, "S": S, "K": w.K, "io_dtype": w.dtype, "out_dtype": w.dtype},
-        "roofline": roof, "cpu_baseline": cpu, "measured_peaks": peaks, "dense_sdpa": dense,
+        "roofline": roof, "cpu_baseline": cpu, "measured_peaks": peaks, "cold": cold, "dense_sdpa": dense,
         "dense_own_kernels": dense_mine, "stages": stages,
     }
     print(json.dumps(line))
