@@ -361,3 +361,27 @@ def test_layer_ragged_length_vs_oracle(case, mode, dev):
         gq, gk, gv = orc.ragged_backward(fw, f64(dOc[b, h]))
         for got, want, n in ((dq, gq, "dQ"), (dk, gk, "dK"), (dv, gv, "dV")):
             _close(f64(got[b, h]), want, tol_for(case, want, case.out), f"{case.name} h{h} {n}")
+
+
+@pytest.mark.parametrize("mode", ["hold", "span"])
+@pytest.mark.parametrize("name", ["bf16-d128-ragged", "bf16-bursts-bf16out"])
+def test_autograd_wrapper_matches_layer_calls(name, mode, dev):
+    """torch.autograd through lighthouse_attention gives the outputs and
+    gradients of the direct lh_layer_fwd / lh_layer_bwd calls, bitwise, and
+    the gradient of a weighted sum of O is dO through the layer backward."""
+    from sparse_long_context_amd.layer import lighthouse_attention
+    case = [c for c in CASES if c.name == name][0]
+    Q, K, V, dO = (t.to(dev) for t in inputs(case))
+    c = _ctx(case, Q, scatter_mode=mode)
+    out = c.out
+    o_ref, saved = ops.layer_fwd(c, Q, K, V)
+    g_ref = ops.layer_bwd(c, saved, dO.to(out))
+    q, k, v = (t.clone().requires_grad_(True) for t in (Q, K, V))
+    o = lighthouse_attention(q, k, v, case.p, case.L, case.S, out_dtype=out, scatter_mode=mode)
+    o.backward(dO.to(out))
+    torch.cuda.synchronize()
+    assert o.dtype == out and torch.equal(o.detach(), o_ref)
+    # autograd hands each gradient back in its input's dtype
+    for got, want, n in zip((q.grad, k.grad, v.grad), g_ref, ("dq", "dk", "dv")):
+        assert got is not None and got.dtype == Q.dtype, n
+        assert torch.equal(got, want.to(Q.dtype)), n
