@@ -33,21 +33,6 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const bf16_t *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
 }
 
-// two 4-element (8-byte) pieces -> one operand
-__device__ __forceinline__ bf16x8 ld_bf16x4x2(const bf16_t *p0, const bf16_t *p1) {
-  const uint2 a = *reinterpret_cast<const uint2 *>(p0);
-  const uint2 b = *reinterpret_cast<const uint2 *>(p1);
-  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-}
-
-// 8 accumulator values acc[o .. o+7] -> bf16 operand (round to nearest even)
-__device__ __forceinline__ bf16x8 pack_bf16x8(const f32x16 &acc, int o) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (__bf16)acc[o + e];
-  return r;
-}
-
 // the same values as a two-term split: hi = bf16(x), lo = bf16(x - hi); the
 // pair carries about 16 significant bits, so a product taken as
 // hi*B + lo*B loses far less than one rounding of x to bf16
@@ -144,20 +129,11 @@ __device__ __forceinline__ void pin(const f32x16 &x) { asm volatile("" ::"a"(x))
 // the same, for a tile that stays in VGPRs
 __device__ __forceinline__ void pin_v(const f32x16 &x) { asm volatile("" ::"v"(x)); }
 
-// Issue-order prescriptions for the scheduler, within one fenced region:
-// NM times one MFMA followed by NR LDS reads (reads started early, under
-// MFMAs that do not need them), or by NV VALU instructions (transcendentals
-// included).  Groups the region cannot fill are skipped.
-template <int NM, int NR>
-__device__ __forceinline__ void sched_mfma_reads() {
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);   // DS read
-  }
-}
-// NM MFMAs, the first RG of them each followed by NR LDS reads, every one
-// followed by NV VALU instructions (NV = 0: VALU left unconstrained)
+// Issue-order prescription for the scheduler, within one fenced region: NM
+// MFMAs, the first RG of them each followed by NR LDS reads (reads started
+// early, under MFMAs that do not need them), every one followed by NV VALU
+// instructions (transcendentals included; NV = 0: VALU left unconstrained).
+// Groups the region cannot fill are skipped.
 template <int NM, int RG, int NR, int NV>
 __device__ __forceinline__ void sched_mix() {
 #pragma unroll
@@ -165,14 +141,6 @@ __device__ __forceinline__ void sched_mix() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (i < RG) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
     if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);
-  }
-}
-template <int NM, int NV>
-__device__ __forceinline__ void sched_mfma_valu() {
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);   // VALU and transcendental
   }
 }
 
