@@ -32,10 +32,10 @@
  *    T = (p^L - 1)/(p - 1) entries per stratum, k_s = K / n_c ranked entries
  *    per stratum, S = K + n_c subsequence rows.
  *  - Streams: all work is ordered on `stream` (a hipStream_t; NULL is the
- *    null stream) and is asynchronous.  The two layer calls also run one
- *    independent kernel on a second stream of the device that the library
+ *    null stream) and is asynchronous.  The two layer calls also run some
+ *    independent kernels on a second stream of the device that the library
  *    keeps (default priority), forked from `stream` and joined back to it by
- *    events, so that it is complete whenever `stream`'s work is.  No call
+ *    events, so that they are complete whenever `stream`'s work is.  No call
  *    synchronises or reads device memory back to the host.
  *  - Outputs are overwritten, never accumulated.
  *  - Errors: every call validates its dims and pointers first and returns a
@@ -43,7 +43,7 @@
  *    failed launch returns LH_ERR_HIP.  No C++ exception crosses the ABI.
  *  - Concurrency: calls are reentrant; the library has no mutable global
  *    state apart from a per-device property cache and a per-device second
- *    stream with two events, each created once under a lock and kept until
+ *    stream with three events, each created once under a lock and kept until
  *    the process ends.
  *  - Determinism: every kernel is free of atomics on floating-point data;
  *    results are bitwise reproducible run to run.

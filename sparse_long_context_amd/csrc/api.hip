@@ -127,26 +127,28 @@ struct Carver {
   bool ok() const { return off <= cap; }
 };
 
-// A second stream of each device (default priority, non-blocking) and two
+// A second stream of each device (default priority, non-blocking) and three
 // events, created on first use and kept until the process ends: the layer
-// forward forks the V pyramid onto it (beside the selection), the layer
-// backward the pooling adjoint of dK and dV (beside the dQ kernel), and each
-// joins it back.  The mutex keeps each fork/join sequence whole when several
-// host threads call on one device.
+// forward forks the V pyramid and V's gather onto it (beside the selection
+// and the Q, K gather), the layer backward the pooling adjoint of dK and dV
+// (beside the dQ kernel), and each joins it back.  The mutex keeps each
+// fork/join sequence whole when several host threads call on one device.
 constexpr int kMaxDevices = 64;
 static std::mutex g_side_mu;
 static hipStream_t g_side[kMaxDevices];
-static hipEvent_t g_fork[kMaxDevices], g_join[kMaxDevices];
+static hipEvent_t g_fork[kMaxDevices], g_mid[kMaxDevices], g_join[kMaxDevices];
 static bool g_side_ok[kMaxDevices];
 
 // call with g_side_mu held
-static lh_status side_stream(hipStream_t *s, hipEvent_t *fork, hipEvent_t *join) {
+static lh_status side_stream(hipStream_t *s, hipEvent_t *fork, hipEvent_t *join,
+                             hipEvent_t *mid = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LH_ERR_HIP;
   if (!g_side_ok[dev]) {
     if (hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking) != hipSuccess)
       return LH_ERR_HIP;
     if (hipEventCreateWithFlags(&g_fork[dev], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&g_mid[dev], hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&g_join[dev], hipEventDisableTiming) != hipSuccess)
       return LH_ERR_HIP;
     g_side_ok[dev] = true;
@@ -154,6 +156,7 @@ static lh_status side_stream(hipStream_t *s, hipEvent_t *fork, hipEvent_t *join)
   *s = g_side[dev];
   *fork = g_fork[dev];
   *join = g_join[dev];
+  if (mid) *mid = g_mid[dev];
   return LH_OK;
 }
 
@@ -510,26 +513,31 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
     v = vp;
   }
   if (!c.ok()) return LH_ERR_WORKSPACE;
-  // Q and K (pyramids and scores), then the V pyramid on the side stream
-  // beside the selection, which needs only the scores
+  // Q and K (pyramids and scores); then, on the side stream, the V pyramid
+  // beside the selection (which needs only the scores), and V's gather once
+  // the selection is there, beside the Q, K gather
   LH_TRY(launch_pyramid_score(g, q, k, nullptr, s->pq, s->pk, nullptr, s->sq, s->sk, st));
   {
     std::lock_guard<std::mutex> lock(g_side_mu);
     hipStream_t side;
-    hipEvent_t fork, join;
-    LH_TRY(side_stream(&side, &fork, &join));
+    hipEvent_t fork, mid, join;
+    LH_TRY(side_stream(&side, &fork, &join, &mid));
     if (hipEventRecord(fork, st) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess)
       return LH_ERR_HIP;
     LH_TRY(launch_pyramid_score(g, nullptr, nullptr, v, nullptr, nullptr, s->pv, nullptr, nullptr,
                                 side));
-    if (hipEventRecord(join, side) != hipSuccess) return LH_ERR_HIP;
     LH_TRY(launch_select(g, s->sq, s->sk, s->sel_idx, s->sel_anchor, s->sel_flags, s->row_of,
                          st));
+    if (hipEventRecord(mid, st) != hipSuccess || hipStreamWaitEvent(side, mid, 0) != hipSuccess)
+      return LH_ERR_HIP;
+    const void *src[3] = {q, k, v}, *psrc[3] = {s->pq, s->pk, s->pv};
+    void *dst[3] = {s->qs, s->ks, s->vs};
+    LH_TRY(launch_gather(g, src, psrc, s->sel_idx, dst, side, 2, 1));
+    if (hipEventRecord(join, side) != hipSuccess) return LH_ERR_HIP;
+    LH_TRY(launch_gather(g, src, psrc, s->sel_idx, dst, st, 0, 2));
     if (hipStreamWaitEvent(st, join, 0) != hipSuccess) return LH_ERR_HIP;
   }
   const bool bf = g.io == LH_BF16;
-  LH_TRY(gather_impl(g, q, k, v, s->pq, s->pk, s->pv, s->sel_idx, s->qs, s->ks, s->vs, nullptr,
-                     nullptr, nullptr, st));
   // bf16 I/O in hold mode: the attention kernel also writes the output
   // under the causal hold (the scatter stage fused into its epilogue)
   const bool fused = bf && g.mode != LH_SCATTER_SPAN;

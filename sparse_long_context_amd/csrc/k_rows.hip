@@ -24,11 +24,12 @@ struct GatherArgs {
   const int32_t *sel_idx;
   int64_t N, E, S;
   int32_t d;
+  int32_t z0;   // first tensor of blockIdx.z = 0
 };
 
 template <typename T, int CPR>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
-  const int z = blockIdx.z;
+  const int z = a.z0 + blockIdx.z;
   const int64_t bh = blockIdx.y;
   const int c = threadIdx.x % CPR;
   const int64_t j = (int64_t)blockIdx.x * (256 / CPR) + threadIdx.x / CPR;
@@ -49,12 +50,14 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 }
 
 lh_status launch_gather(const Geo &g, const void *const src[3], const void *const psrc[3],
-                        const int32_t *sel_idx, void *const dst[3], hipStream_t st) {
+                        const int32_t *sel_idx, void *const dst[3], hipStream_t st, int z0,
+                        int nz) {
+  if (z0 < 0 || nz < 1 || z0 + nz > 3) return LH_ERR_INVALID_ARG;
   GatherArgs a;
   for (int i = 0; i < 3; ++i) { a.src[i] = src[i]; a.psrc[i] = psrc[i]; a.dst[i] = dst[i]; }
-  a.sel_idx = sel_idx; a.N = g.N; a.E = g.E; a.S = g.S; a.d = g.d;
+  a.sel_idx = sel_idx; a.N = g.N; a.E = g.E; a.S = g.S; a.d = g.d; a.z0 = z0;
   const int cpr = g.d / 8;
-  dim3 grid(cdiv(g.S, 256 / cpr), (unsigned)g.BH(), 3);
+  dim3 grid(cdiv(g.S, 256 / cpr), (unsigned)g.BH(), (unsigned)nz);
   if (g.io == LH_BF16) {
     if (g.d == 128) hipLaunchKernelGGL((gather_kernel<bf16_t, 16>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((gather_kernel<bf16_t, 8>), grid, dim3(256), 0, st, a);

@@ -119,8 +119,10 @@ lh_status launch_select(const Geo &g, const float *sq, const float *sk, int32_t 
                         hipStream_t st);
 lh_status check_select_supported(const Geo &g);
 
+// tensors z0 .. z0 + nz - 1 of the three (0 q, 1 k, 2 v)
 lh_status launch_gather(const Geo &g, const void *const src[3], const void *const psrc[3],
-                        const int32_t *sel_idx, void *const dst[3], hipStream_t st);
+                        const int32_t *sel_idx, void *const dst[3], hipStream_t st, int z0 = 0,
+                        int nz = 3);
 // rows [BH, S, d] bf16 -> [BH, d, Sp] bf16 with zeroed padding
 lh_status launch_transpose(const Geo &g, const void *rows, void *tr, hipStream_t st);
 // os is float32; o has the output type
