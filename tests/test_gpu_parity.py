@@ -385,3 +385,44 @@ def test_autograd_wrapper_matches_layer_calls(name, mode, dev):
     for got, want, n in zip((q.grad, k.grad, v.grad), g_ref, ("dq", "dk", "dv")):
         assert got is not None and got.dtype == Q.dtype, n
         assert torch.equal(got, want.to(Q.dtype)), n
+
+
+def test_layer_from_two_threads_on_two_streams(dev):
+    """Two host threads run lh_layer_fwd + lh_layer_bwd at the same time on
+    two streams of one device (the calls share the library's second stream
+    and its events); each result equals the sequential one, bitwise."""
+    import threading
+    case = [c for c in CASES if c.name == "bf16-bursts-bf16out"][0]
+    Q, K, V, dO = (t.to(dev) for t in inputs(case))
+    c = _ctx(case, Q)
+    ref_o, s = ops.layer_fwd(c, Q, K, V)
+    ref_g = ops.layer_bwd(c, s, dO.to(c.out))
+    torch.cuda.synchronize()
+    results, errors = [None, None], []
+
+    def run(i):
+        try:
+            st = torch.cuda.Stream(device=dev)   # default priority
+            with torch.cuda.stream(st):
+                outs = []
+                for _ in range(3):
+                    o, sv = ops.layer_fwd(c, Q, K, V)
+                    g = ops.layer_bwd(c, sv, dO.to(c.out))
+                    outs.append((o, g))
+            st.synchronize()
+            results[i] = outs
+        except Exception as e:   # reported below
+            errors.append(repr(e))
+
+    ts = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for outs in results:
+        for o, g in outs:
+            assert torch.equal(o, ref_o)
+            for a, b in zip(g, ref_g):
+                assert torch.equal(a, b)
