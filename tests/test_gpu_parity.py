@@ -213,6 +213,16 @@ def test_layer_matches_stages_and_is_deterministic(case, dev):
     assert torch.equal(o1, r["o"])
     for a, n in zip(g1, ("dq", "dk", "dv")):
         assert torch.equal(a, r[n]), n
+    # everything the layer forward saves for the backward (pyramids, scores,
+    # selection, gathered rows) equals the separate stages' outputs, bitwise
+    for n, m in (("sq", "sq"), ("sk", "sk"), ("pq", "pq"), ("pk", "pk"), ("pv", "pv"),
+                 ("sel_idx", "sel_idx"), ("sel_anchor", "anchor"), ("sel_flags", "flags"),
+                 ("row_of", "row_of"), ("qs", "qs"), ("ks", "ks"), ("vs", "vs")):
+        for sv in (s1, s2):
+            if sv[n] is None:
+                assert r[m] is None or r[m].numel() == 0, n
+            else:
+                assert torch.equal(sv[n], r[m]), n
 
 
 @pytest.mark.parametrize("case", CASES, ids=ids)
