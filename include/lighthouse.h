@@ -92,6 +92,19 @@ typedef int32_t lh_status;
 #define LH_SIGMA_MAX     1   /* max(sq, sk)                                 */
 #define LH_SIGMA_PRODUCT 2   /* float32(sq * sk)                            */
 
+/* lh_dims.strata_mode: how a stratum's k_s ranked entries are shared out
+ * (the pages stratify the top-K against collapse and also call it joint
+ * across levels; which of the two governs the levels is open).  Either way a
+ * stratum is one coarsest cell with its subtree and its root is kept. */
+#define LH_STRATA_JOINT     0   /* one ranking over levels 0..L-2, the default */
+#define LH_STRATA_PER_LEVEL 1   /* a quota per level, ranked within the level:
+                                   levels L-2 down to 1 in turn take
+                                   min(level size, remaining / levels left),
+                                   level 0 takes the rest (lh_validate
+                                   rejects a budget where that would not fit
+                                   in level 0; none with k_s <= T-1 was found
+                                   for p <= 8, L <= 7)                      */
+
 typedef void *lh_stream;     /* a hipStream_t */
 
 /* Problem statement of one layer call (explainer section 2.A-2.C: sequence
@@ -102,7 +115,8 @@ typedef void *lh_stream;     /* a hipStream_t */
  *   E < 2^31, d in {64, 128}, io_dtype/out_dtype in {LH_F32, LH_BF16},
  *   out_dtype == LH_F32 when io_dtype == LH_F32, scale >= 0 and finite,
  *   scatter_mode in {LH_SCATTER_HOLD, LH_SCATTER_SPAN},
- *   sigma_mode in {LH_SIGMA_SUM, LH_SIGMA_MAX, LH_SIGMA_PRODUCT}.
+ *   sigma_mode in {LH_SIGMA_SUM, LH_SIGMA_MAX, LH_SIGMA_PRODUCT},
+ *   strata_mode in {LH_STRATA_JOINT, LH_STRATA_PER_LEVEL}.
  * The geometry (levels, strata, E, n_c, ...) is that of N rounded up to
  * whole coarsest cells of B_c = p^(L-1) tokens: n_c = ceil(N / B_c).  When N
  * is not a multiple of B_c (the pages assume whole cells; the reading taken
@@ -124,6 +138,7 @@ typedef struct lh_dims {
   float scale;        /* softmax scale; 0 selects 1/sqrt(d)                  */
   int32_t scatter_mode; /* LH_SCATTER_HOLD (0) or LH_SCATTER_SPAN (1)        */
   int32_t sigma_mode;   /* LH_SIGMA_SUM (0), LH_SIGMA_MAX (1), LH_SIGMA_PRODUCT */
+  int32_t strata_mode;  /* LH_STRATA_JOINT (0) or LH_STRATA_PER_LEVEL (1)     */
 } lh_dims;
 
 /* Buffers the forward fills and the backward reads (all caller-owned).
@@ -217,7 +232,8 @@ lh_status lh_pyramid_score(const lh_dims *dims, const void *q, const void *k,
  * Per (b, h) and stratum m (coarsest entry (L-1, m) with its subtree): keep
  * the root and the k_s entries of levels 0..L-2 with the largest
  * sigma = float32(sq + sk), ties to the lower flat index (finer level first,
- * then lower position).  Rows of stratum m are [m (k_s+1), (m+1)(k_s+1)),
+ * then lower position); with LH_STRATA_PER_LEVEL, level l's quota of them
+ * is ranked among level l's entries only (same key).  Rows of stratum m are [m (k_s+1), (m+1)(k_s+1)),
  * ordered by (anchor, level) ascending.  Out:
  *   sel_idx, sel_anchor [B,H,S] int32; sel_flags [B,H,S] uint8 (REDUNDANT:
  *   all p children selected or redundant; LEADER: first row or anchor

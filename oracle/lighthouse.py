@@ -36,7 +36,7 @@ Notation (one batch element b, one head h):
   subsequence length S = K + n_c.
 
 Parity pins for every function live in tests/test_oracle_*.py.  Conventions
-R-5, R-7, R-9, R-11, R-12, R-14 and R-14' are readings of open points: they are
+R-5, R-7, R-7', R-9, R-11, R-12, R-14 and R-14' are readings of open points: they are
 pinned by invariants and special cases, not by a value the pages print
 ("parity unpinned" by the pages themselves).
 """
@@ -261,7 +261,28 @@ def stratum_members(g: Geometry, m: int):
     return np.concatenate(out)
 
 
-def select(sig, g: Geometry, near_tie_rel: float = 1e-6):
+def level_quotas(g: Geometry):
+    """R-7' (the per-level reading of "stratified", an ablation of R-7): the
+    k_s ranked entries of a stratum are shared out as quotas over levels
+    0..L-2.  Going from the coarsest ranked level L-2 down to level 1, each
+    level takes an equal share of what is left, floor(left / levels left),
+    but no more than the p**(L-1-l) entries it has in the stratum; level 0
+    takes the remainder, which must fit in its B_c entries.  Returns the
+    list of quotas indexed by level (length L-1)."""
+    q = [0] * max(g.L - 1, 0)
+    left = g.k_s
+    for l in range(g.L - 2, 0, -1):
+        have = g.Bc // g.p ** l
+        q[l] = min(have, left // (l + 1))
+        left -= q[l]
+    if g.L >= 2:
+        if left > g.Bc:
+            raise ValueError("per-level quotas: level 0 cannot hold the remainder")
+        q[0] = left
+    return q
+
+
+def select(sig, g: Geometry, near_tie_rel: float = 1e-6, strata="joint"):
     """Stratified joint top-K with the coarsest level always kept.
 
     [EXP-2B]: a top-K chosen jointly across all levels.  [NEWS]: the top-K is
@@ -288,6 +309,8 @@ def select(sig, g: Geometry, near_tie_rel: float = 1e-6):
     near_tie (R-10): the last selected and first unselected candidate of a
          stratum differ by at most near_tie_rel * (largest sigma of the
          stratum); index mismatches are only excusable in such strata.
+    strata: "joint" (R-7) or "per_level" (R-7', level_quotas): the same key
+         ranks each level's entries of the stratum for that level's quota.
     """
     g.check()
     sig = np.asarray(sig, dtype=np.float32)
@@ -296,20 +319,29 @@ def select(sig, g: Geometry, near_tie_rel: float = 1e-6):
     sel_mask = np.zeros(E, dtype=bool)
     near = np.zeros(g.n_c, dtype=bool)
     root0 = g.level_offsets[-1]
+    if strata not in ("joint", "per_level"):
+        raise ValueError(f"strata {strata!r}")
+    quotas = level_quotas(g) if strata == "per_level" else None
     for m in range(g.n_c):
         members = stratum_members(g, m)
         root = root0 + m
-        cand = members[members != root]
-        # ranking: sigma descending, then flat index ascending
-        order = np.lexsort((cand, -sig[cand].astype(np.float64)))
-        chosen = cand[order[:k_s]]
-        sel_mask[chosen] = True
         sel_mask[root] = True
-        if 0 < k_s < len(cand):
-            s_last = float(sig[cand[order[k_s - 1]]])
-            s_next = float(sig[cand[order[k_s]]])
-            smax = float(sig[members].max())
-            near[m] = (s_last - s_next) <= near_tie_rel * smax
+        smax = float(sig[members].max())
+        if quotas is None:
+            groups = [(members[members != root], k_s)]
+        else:
+            groups = []
+            for l in range(g.L - 1):
+                per = g.Bc // g.p ** l
+                groups.append((g.level_offsets[l] + m * per + np.arange(per), quotas[l]))
+        for cand, k in groups:
+            # ranking: sigma descending, then flat index ascending
+            order = np.lexsort((cand, -sig[cand].astype(np.float64)))
+            sel_mask[cand[order[:k]]] = True
+            if 0 < k < len(cand):
+                s_last = float(sig[cand[order[k - 1]]])
+                s_next = float(sig[cand[order[k]]])
+                near[m] |= (s_last - s_next) <= near_tie_rel * smax
 
     # redundancy, bottom-up over levels
     sizes, offs = g.level_sizes, g.level_offsets
@@ -546,18 +578,19 @@ class HeadForward:
 
 
 def head_forward(Q, K_, V, g: Geometry, scale=None, store=None, selection=None,
-                 scatter_mode="hold", sigma_mode="sum"):
+                 scatter_mode="hold", sigma_mode="sum", strata_mode="joint"):
     """One head of the layer: pyramid -> scores -> selection -> gather ->
     attention -> scatter.  `selection` (a Selection) replaces the computed
     one, so downstream stages can be checked on a given selection.
     scatter_mode: "hold" (R-14, causal hold) or "span" (R-14', span
-    broadcast).  sigma_mode: how the two scores combine (R-5)."""
+    broadcast).  sigma_mode: how the two scores combine (R-5).  strata_mode:
+    "joint" (R-7) or "per_level" (R-7')."""
     g.check()
     d = np.asarray(Q).shape[1]
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     sQ, sK = scores(Q, K_, g)
     sig = sigma(sQ, sK, sigma_mode)
-    sel = select(sig, g) if selection is None else selection
+    sel = select(sig, g, strata=strata_mode) if selection is None else selection
     Ql, Kl, Vl = (pyramid(X, g, store) for X in (Q, K_, V))
     QS, KS, VS = gather(Ql, sel.sel_idx), gather(Kl, sel.sel_idx), gather(Vl, sel.sel_idx)
     OS, LSE = attention_fwd(QS, KS, VS, sel.sel_flags, scale)
@@ -625,11 +658,12 @@ def ragged_backward(fw: HeadForward, dO):
 
 
 def layer_forward(Q, K_, V, p, L, K, scale=None, store=None, scatter_mode="hold",
-                  sigma_mode="sum"):
+                  sigma_mode="sum", strata_mode="joint"):
     """[B, H, N, d] arrays -> list over (b, h) of HeadForward."""
     Q = np.asarray(Q)
     B, H, N, _ = Q.shape
     g = Geometry(N, p, L, K).check()
     return [[head_forward(Q[b, h], K_[b, h], V[b, h], g, scale, store,
-                          scatter_mode=scatter_mode, sigma_mode=sigma_mode)
+                          scatter_mode=scatter_mode, sigma_mode=sigma_mode,
+                          strata_mode=strata_mode)
              for h in range(H)] for b in range(B)]

@@ -18,6 +18,7 @@ LH_F32, LH_BF16 = 0, 1
 LH_ROW_REDUNDANT, LH_ROW_LEADER = 1, 2
 LH_SCATTER_HOLD, LH_SCATTER_SPAN = 0, 1
 LH_SIGMA_SUM, LH_SIGMA_MAX, LH_SIGMA_PRODUCT = 0, 1, 2
+LH_STRATA_JOINT, LH_STRATA_PER_LEVEL = 0, 1
 
 
 class LighthouseError(RuntimeError):
@@ -30,7 +31,8 @@ class Dims(C.Structure):
     _fields_ = [("B", C.c_int64), ("N", C.c_int64), ("H", C.c_int32), ("d", C.c_int32),
                 ("p", C.c_int32), ("L", C.c_int32), ("K", C.c_int64), ("S", C.c_int64),
                 ("io_dtype", C.c_int32), ("out_dtype", C.c_int32), ("scale", C.c_float),
-                ("scatter_mode", C.c_int32), ("sigma_mode", C.c_int32)]
+                ("scatter_mode", C.c_int32), ("sigma_mode", C.c_int32),
+                ("strata_mode", C.c_int32)]
 
 
 class Saved(C.Structure):
@@ -119,9 +121,10 @@ def check(status: int, what: str):
 
 
 def make_dims(B, N, H, d, p, L, K, S, io_dtype=LH_BF16, out_dtype=None, scale=0.0,
-              scatter_mode=LH_SCATTER_HOLD, sigma_mode=LH_SIGMA_SUM) -> Dims:
+              scatter_mode=LH_SCATTER_HOLD, sigma_mode=LH_SIGMA_SUM,
+              strata_mode=LH_STRATA_JOINT) -> Dims:
     return Dims(B, N, H, d, p, L, K, S, io_dtype, io_dtype if out_dtype is None else out_dtype,
-                float(scale), int(scatter_mode), int(sigma_mode))
+                float(scale), int(scatter_mode), int(sigma_mode), int(strata_mode))
 
 
 def sizes(dims: Dims) -> Sizes:

@@ -27,6 +27,8 @@ lh_status make_geo(const lh_dims *dm, Geo *g) {
   if (dm->sigma_mode != LH_SIGMA_SUM && dm->sigma_mode != LH_SIGMA_MAX &&
       dm->sigma_mode != LH_SIGMA_PRODUCT)
     return LH_ERR_INVALID_ARG;
+  if (dm->strata_mode != LH_STRATA_JOINT && dm->strata_mode != LH_STRATA_PER_LEVEL)
+    return LH_ERR_INVALID_ARG;
   if (dm->L >= kMaxLevels) return LH_ERR_UNSUPPORTED;
   if (!(dm->scale >= 0.0f) || !isfinite(dm->scale)) return LH_ERR_INVALID_ARG;
   if ((dm->io_dtype != LH_F32 && dm->io_dtype != LH_BF16) ||
@@ -37,6 +39,7 @@ lh_status make_geo(const lh_dims *dm, Geo *g) {
   g->K = dm->K; g->S = dm->S; g->io = dm->io_dtype; g->out = dm->out_dtype;
   g->mode = dm->scatter_mode;
   g->sigma = dm->sigma_mode;
+  g->strata = dm->strata_mode;
   g->pw[0] = 1;
   for (int l = 1; l <= g->L; ++l)
     if (!mul_ok(g->pw[l - 1], g->p, lim, &g->pw[l])) return LH_ERR_INVALID_ARG;
@@ -58,6 +61,19 @@ lh_status make_geo(const lh_dims *dm, Geo *g) {
   if (g->K < 0 || g->K % g->n_c) return LH_ERR_INVALID_ARG;
   g->k_s = g->K / g->n_c;
   if (g->k_s > g->T - 1) return LH_ERR_INVALID_ARG;
+  if (g->strata == LH_STRATA_PER_LEVEL && g->L >= 2) {
+    // levels L-2 .. 1 in turn take min(their size, remaining / levels left);
+    // level 0 takes what remains, which must fit in it
+    int64_t rem = g->k_s;
+    for (int l = g->L - 2; l >= 1; --l) {
+      const int64_t n = g->Bc / g->pw[l];
+      const int64_t share = rem / (l + 1);
+      g->quota[l] = share < n ? share : n;
+      rem -= g->quota[l];
+    }
+    if (rem > g->Bc) return LH_ERR_INVALID_ARG;
+    g->quota[0] = rem;
+  }
   if (g->S != g->K + g->n_c) return LH_ERR_INVALID_ARG;
   if (g->E >= ((int64_t)1 << 31) || g->S >= ((int64_t)1 << 31)) return LH_ERR_UNSUPPORTED;
   if (g->BH() > 65535) return LH_ERR_UNSUPPORTED;

@@ -10,7 +10,8 @@
 //
 // Readings (stated in the design notes): a stratum is one coarsest cell with
 // its subtree; its root is always kept and k_s = K/n_c further entries are
-// taken by sigma descending, ties to the lower flat index, with sigma =
+// taken by sigma descending, ties to the lower flat index (or, by
+// strata_mode, a quota per level ranked within the level), with sigma =
 // float32(sq + sk) (or, by sigma_mode, max(sq, sk) or float32(sq * sk));
 // rows follow (anchor, level) ascending; an entry is REDUNDANT when all its
 // children are selected or redundant; a LEADER is the first row at its anchor.
@@ -39,7 +40,8 @@ struct SelArgs {
   int32_t *sel_idx, *sel_anchor, *row_of;
   uint8_t *sel_flags;
   int64_t N, E, S, Bc, k_s;
-  int32_t p, L, T, sigma;
+  int32_t p, L, T, sigma, strata;
+  int64_t quota[kMaxLevels];        // per-level quotas (LH_STRATA_PER_LEVEL)
   int64_t lsize[kMaxLevels], loff[kMaxLevels], pw[kMaxLevels + 1];
   int32_t cstart[kMaxLevels + 1];   // first candidate index of each level
   int32_t tsub[kMaxLevels];         // subtree size of a level-l entry
@@ -110,16 +112,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
   }
   __syncthreads();
 
-  // 2. selection among candidates 0..T-2 (the root T-1 is always kept)
-  if (k_s >= ncand) {
-    for (int ci = tid; ci < ncand; ci += kSelThreads) st[ci] = 1;
-  } else if (k_s > 0) {
+  // 2. selection among candidates 0..T-2 (the root T-1 is always kept):
+  // the k largest keys of candidates [c0, c1), exact ties to the lower
+  // candidate index; one range of k_s (joint ranking) or one per level
+  auto select_range = [&](int c0r, int c1r, int k) {
+    const int nr = c1r - c0r;
+    if (k >= nr) {
+      for (int ci = c0r + tid; ci < c1r; ci += kSelThreads) st[ci] = 1;
+      return;
+    }
+    if (k <= 0) return;
     uint32_t prefix = 0, pmask = 0;
-    int remaining = (int)k_s;
+    int remaining = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
       hist[tid] = 0;
       __syncthreads();
-      for (int ci = tid; ci < ncand; ci += kSelThreads) {
+      for (int ci = c0r + tid; ci < c1r; ci += kSelThreads) {
         const uint32_t kk = key[ci];
         if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255], 1);
       }
@@ -141,18 +149,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
     const uint32_t thr = prefix;
     const int need = remaining;
     // first `need` candidates (in candidate order) with key == thr
-    const int chunk = (ncand + kSelThreads - 1) / kSelThreads;
-    const int c0 = tid * chunk, c1 = min(ncand, c0 + chunk);
+    const int chunk = (nr + kSelThreads - 1) / kSelThreads;
+    const int q0 = c0r + tid * chunk, q1 = min(c1r, q0 + chunk);
     int eq = 0;
-    for (int ci = c0; ci < c1; ++ci) eq += key[ci] == thr;
+    for (int ci = q0; ci < q1; ++ci) eq += key[ci] == thr;
     int tot;
     int rank = block_excl_scan(eq, &tot, wsum);
-    for (int ci = c0; ci < c1; ++ci) {
+    for (int ci = q0; ci < q1; ++ci) {
       const uint32_t kk = key[ci];
       bool s = kk > thr;
       if (kk == thr) s = rank++ < need;
       st[ci] = s ? 1 : 0;
     }
+  };
+  if (a.strata == LH_STRATA_PER_LEVEL) {
+    for (int l = 0; l + 1 < a.L; ++l) select_range(a.cstart[l], a.cstart[l + 1], (int)a.quota[l]);
+  } else {
+    select_range(0, ncand, (int)k_s);
   }
   if (tid == 0) st[ncand] = 1;   // root
   __syncthreads();
@@ -219,7 +232,8 @@ lh_status launch_select(const Geo &g, const float *sq, const float *sk, int32_t 
   a.sq = sq; a.sk = sk; a.sel_idx = sel_idx; a.sel_anchor = sel_anchor; a.row_of = row_of;
   a.sel_flags = sel_flags;
   a.N = g.N; a.E = g.E; a.S = g.S; a.Bc = g.Bc; a.k_s = g.k_s;
-  a.p = g.p; a.L = g.L; a.T = (int32_t)g.T; a.sigma = g.sigma;
+  a.p = g.p; a.L = g.L; a.T = (int32_t)g.T; a.sigma = g.sigma; a.strata = g.strata;
+  for (int l = 0; l < kMaxLevels; ++l) a.quota[l] = g.quota[l];
   for (int l = 0; l < kMaxLevels; ++l) { a.lsize[l] = g.lsize[l]; a.loff[l] = g.loff[l]; }
   for (int l = 0; l <= kMaxLevels; ++l) a.pw[l] = g.pw[l];
   int cs = 0;

@@ -23,6 +23,8 @@ struct Geo {
                                  // whole coarsest cells: the layer pads with zero rows)
   int32_t mode;                  // LH_SCATTER_HOLD or LH_SCATTER_SPAN
   int32_t sigma;                 // LH_SIGMA_SUM, LH_SIGMA_MAX or LH_SIGMA_PRODUCT
+  int32_t strata;                // LH_STRATA_JOINT or LH_STRATA_PER_LEVEL
+  int64_t quota[kMaxLevels];     // per-level quotas of k_s (LH_STRATA_PER_LEVEL)
   float scale;                   // softmax scale (1/sqrt(d) when dims say 0)
   int64_t lsize[kMaxLevels];     // N / p^l
   int64_t loff[kMaxLevels];      // flat offset of level l

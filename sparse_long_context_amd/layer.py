@@ -14,8 +14,9 @@ from . import ops
 
 class LighthouseAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, p, L, S, out_dtype, scale, scatter_mode, sigma_mode):
-        c = ops.Ctx(ops.make_dims(q, p, L, S, out_dtype, scale, scatter_mode, sigma_mode))
+    def forward(ctx, q, k, v, p, L, S, out_dtype, scale, scatter_mode, sigma_mode, strata_mode):
+        c = ops.Ctx(ops.make_dims(q, p, L, S, out_dtype, scale, scatter_mode, sigma_mode,
+                                  strata_mode))
         o, saved = ops.layer_fwd(c, q.contiguous(), k.contiguous(), v.contiguous())
         ctx.c = c
         ctx.saved = saved
@@ -24,13 +25,16 @@ class LighthouseAttention(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dout):
         dq, dk, dv = ops.layer_bwd(ctx.c, ctx.saved, dout.contiguous().to(ctx.c.out))
-        return dq, dk, dv, None, None, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None, None, None
 
 
 def lighthouse_attention(q, k, v, p: int, L: int, S: int, out_dtype=None, scale: float = 0.0,
-                         scatter_mode: str = "hold", sigma_mode: str = "sum"):
+                         scatter_mode: str = "hold", sigma_mode: str = "sum",
+                         strata_mode: str = "joint"):
     """q, k, v: [B, H, N, d] device tensors (bf16 or float32).  Returns O
     [B, H, N, d] in out_dtype (default: the input dtype).  scatter_mode:
     "hold" (causal hold) or "span" (span broadcast); sigma_mode: how the two
-    scores combine ("sum", "max" or "product")."""
-    return LighthouseAttention.apply(q, k, v, p, L, S, out_dtype, scale, scatter_mode, sigma_mode)
+    scores combine ("sum", "max" or "product"); strata_mode: one ranking
+    across a stratum's levels ("joint") or a quota per level ("per_level")."""
+    return LighthouseAttention.apply(q, k, v, p, L, S, out_dtype, scale, scatter_mode, sigma_mode,
+                                     strata_mode)

@@ -36,10 +36,11 @@ def _need(t, shape, dtype, name):
 
 SCATTER_MODES = {"hold": L.LH_SCATTER_HOLD, "span": L.LH_SCATTER_SPAN}
 SIGMA_MODES = {"sum": L.LH_SIGMA_SUM, "max": L.LH_SIGMA_MAX, "product": L.LH_SIGMA_PRODUCT}
+STRATA_MODES = {"joint": L.LH_STRATA_JOINT, "per_level": L.LH_STRATA_PER_LEVEL}
 
 
 def make_dims(q: torch.Tensor, p: int, L_: int, S: int, out_dtype=None, scale: float = 0.0,
-              scatter_mode: str = "hold", sigma_mode: str = "sum"):
+              scatter_mode: str = "hold", sigma_mode: str = "sum", strata_mode: str = "joint"):
     """Dims of a call on q [B, H, N, d]; K is S minus the n_c kept roots."""
     B, H, N, d = q.shape
     Bc = p ** (L_ - 1)
@@ -47,7 +48,7 @@ def make_dims(q: torch.Tensor, p: int, L_: int, S: int, out_dtype=None, scale: f
     io = LHDT[q.dtype]
     out = io if out_dtype is None else LHDT[out_dtype]
     return L.make_dims(B, N, H, d, p, L_, S - n_c, S, io, out, scale, SCATTER_MODES[scatter_mode],
-                       SIGMA_MODES[sigma_mode])
+                       SIGMA_MODES[sigma_mode], STRATA_MODES[strata_mode])
 
 
 class Ctx:

@@ -88,6 +88,19 @@ def test_validate_sigma_mode(lib):
         assert lib.lh_validate(C.byref(d)) == code, mode
 
 
+def test_validate_strata_mode(lib):
+    d = dims()
+    for mode, code in ((L.LH_STRATA_JOINT, L.LH_OK), (L.LH_STRATA_PER_LEVEL, L.LH_OK),
+                       (2, L.LH_ERR_INVALID_ARG), (-1, L.LH_ERR_INVALID_ARG)):
+        d.strata_mode = mode
+        assert lib.lh_validate(C.byref(d)) == code, mode
+    # the largest budget of the 128K workload's trees is feasible per level
+    d = dims(N=131072, H=8, d=128, p=4, L=6, K=1365 * 128 - 128, S=1365 * 128,
+             io_dtype=L.LH_BF16, out_dtype=L.LH_BF16)
+    d.strata_mode = L.LH_STRATA_PER_LEVEL
+    assert lib.lh_validate(C.byref(d)) == L.LH_OK
+
+
 def test_span_mode_workspace_holds_the_owner_map(lib):
     d = dims(N=131072, H=8, d=128, p=4, L=6, K=8064, S=8192, io_dtype=L.LH_BF16,
              out_dtype=L.LH_BF16)

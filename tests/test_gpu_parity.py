@@ -20,12 +20,13 @@ if torch.cuda.is_available():
     from sparse_long_context_amd import ops
 
 
-def _ctx(case, q, scatter_mode="hold", sigma_mode="sum"):
+def _ctx(case, q, scatter_mode="hold", sigma_mode="sum", strata_mode="joint"):
     out = torch.float32 if case.out == "f32" else torch.bfloat16
     if case.dtype == "f32":
         out = torch.float32
     return ops.Ctx(ops.make_dims(q, case.p, case.L, case.S, out_dtype=out,
-                                 scatter_mode=scatter_mode, sigma_mode=sigma_mode))
+                                 scatter_mode=scatter_mode, sigma_mode=sigma_mode,
+                                 strata_mode=strata_mode))
 
 
 @pytest.fixture(scope="module")
@@ -329,6 +330,51 @@ def test_layer_product_sigma_vs_oracle(case, dev):
     for b, h in bh_pairs(case):
         fw = orc.head_forward(f64(Q[b, h]), f64(K[b, h]), f64(V[b, h]), g, store=store_of(case),
                               sigma_mode="product")
+        assert np.array_equal(saved["sel_idx"][b, h].cpu().numpy(), fw.sel.sel_idx)
+        _close(f64(o[b, h]), fw.O, tol_for(case, fw.O, case.out), f"{case.name} h{h} O")
+        gq, gk, gv = orc.head_backward(fw, f64(dOc[b, h]))[:3]
+        for got, want, n in ((dq, gq, "dQ"), (dk, gk, "dK"), (dv, gv, "dV")):
+            _close(f64(got[b, h]), want, tol_for(case, want, case.out), f"{case.name} h{h} {n}")
+
+
+STRATA_CASES = [c for c in CASES if c.name in (
+    "tiny-f32", "bf16-d128-ragged", "bf16-d64-p8-ragged", "bf16-full-selection",
+    "bf16-coarsest-only", "bf16-batch2-p2", "bf16-p3", "bf16-one-stratum")]
+
+
+@pytest.mark.parametrize("case", STRATA_CASES, ids=lambda c: c.name)
+def test_selection_per_level_strata(case, dev):
+    """Per-level quotas (reading R-7', the strata option): the whole
+    selection bit-exact against the oracle's on the same score planes."""
+    r = stages(case, dev)
+    c = _ctx(case, r["Q"], strata_mode="per_level")
+    sel_idx, anchor, flags, row_of = ops.topk_select(c, r["sq"], r["sk"])
+    torch.cuda.synchronize()
+    g = geometry(case)
+    for b, h in bh_pairs(case):
+        sig = orc.sigma(r["sq"][b, h].cpu().numpy(), r["sk"][b, h].cpu().numpy())
+        sel = orc.select(sig, g, strata="per_level")
+        assert np.array_equal(sel_idx[b, h].cpu().numpy(), sel.sel_idx)
+        assert np.array_equal(anchor[b, h].cpu().numpy(), sel.sel_anchor)
+        assert np.array_equal(flags[b, h].cpu().numpy(), sel.sel_flags)
+        assert np.array_equal(row_of[b, h].cpu().numpy(), sel.row_of)
+
+
+@pytest.mark.parametrize("case", [c for c in STRATA_CASES if c.name in ("bf16-d128-ragged",
+                                                                      "bf16-p3")],
+                         ids=lambda c: c.name)
+def test_layer_per_level_strata_vs_oracle(case, dev):
+    """lh_layer_fwd/bwd with strata_mode = per level against the oracle."""
+    Q, K, V, dO = (t.to(dev) for t in inputs(case))
+    c = _ctx(case, Q, strata_mode="per_level")
+    o, saved = ops.layer_fwd(c, Q, K, V)
+    dOc = dO.to(c.out)
+    dq, dk, dv = ops.layer_bwd(c, saved, dOc)
+    torch.cuda.synchronize()
+    g = geometry(case)
+    for b, h in bh_pairs(case):
+        fw = orc.head_forward(f64(Q[b, h]), f64(K[b, h]), f64(V[b, h]), g, store=store_of(case),
+                              strata_mode="per_level")
         assert np.array_equal(saved["sel_idx"][b, h].cpu().numpy(), fw.sel.sel_idx)
         _close(f64(o[b, h]), fw.O, tol_for(case, fw.O, case.out), f"{case.name} h{h} O")
         gq, gk, gv = orc.head_backward(fw, f64(dOc[b, h]))[:3]

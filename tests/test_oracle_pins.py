@@ -270,6 +270,78 @@ def test_selection_dominance_and_order(N, p, L, ks):
     assert np.array_equal(anc // g.Bc, np.repeat(np.arange(g.n_c), ks + 1))
 
 
+# ---------------------------------------------------------------- R-7' per-level quotas
+def test_level_quotas_closed_form():
+    # 128K tokens, p = 4, L = 6, k_s = 63: levels 4, 3, 2, 1 take
+    # min(size, left // levels left) = 4, 14, 15, 15; level 0 the rest, 15
+    assert orc.level_quotas(orc.Geometry(131072, 4, 6, 8064)) == [15, 15, 15, 14, 4]
+    # every budget of small trees: quotas sum to k_s and fit their levels;
+    # a full budget takes every entry
+    for p in (2, 3, 4, 8):
+        for L in (1, 2, 3, 4):
+            Bc = p ** (L - 1)
+            T = sum(p ** l for l in range(L))
+            for ks in range(T):
+                q = orc.level_quotas(orc.Geometry(Bc, p, L, ks))
+                assert len(q) == L - 1 and sum(q) == ks
+                assert all(0 <= q[l] <= Bc // p ** l for l in range(L - 1))
+            full = orc.level_quotas(orc.Geometry(Bc, p, L, T - 1))
+            assert full == [Bc // p ** l for l in range(L - 1)]
+
+
+@pytest.mark.parametrize("N,p,L,ks,ties", [
+    (256, 2, 4, 5, False), (256, 4, 3, 7, True), (512, 8, 3, 20, True),
+    (64, 2, 6, 30, True), (1024, 4, 4, 30, True)])
+def test_per_level_selection_brute_force(N, p, L, ks, ties):
+    """Each level of each stratum holds exactly its quota, and the chosen
+    entries of a level are its first ones in a Python sort by
+    (-sigma, position); root kept; rows ordered as in the joint reading."""
+    g, s, _ = _selection_case(N, p, L, ks, 7, ties)
+    sel = orc.select(s, g, strata="per_level")
+    q = orc.level_quotas(g)
+    chosen = set(sel.sel_idx.tolist())
+    assert len(sel.sel_idx) == g.S and len(chosen) == g.S
+    for m in range(g.n_c):
+        for l in range(L - 1):
+            w = p ** l
+            ents = sorted((-float(s[g.level_offsets[l] + i]), i)
+                          for i in range(m * g.Bc // w, (m + 1) * g.Bc // w))
+            want = {g.level_offsets[l] + i for _, i in ents[:q[l]]}
+            got = {f for f in chosen
+                   if g.level_offsets[l] <= f - m * g.Bc // w < g.level_offsets[l] + g.Bc // w}
+            assert got == want, (m, l)
+        assert g.level_offsets[-1] + m in chosen
+    lev, idx = orc.entry_of_flat(g, sel.sel_idx)
+    anc = (idx + 1) * p ** lev - 1
+    assert np.all(np.diff(anc * 64 + lev) > 0)
+
+
+def test_per_level_is_joint_with_one_ranked_level():
+    # L = 2: level 0 is the only ranked level, so the two readings agree
+    g, s, joint = _selection_case(512, 8, 2, 5, 3, ties=True)
+    per = orc.select(s, g, strata="per_level")
+    for a, b in ((joint.sel_idx, per.sel_idx), (joint.sel_flags, per.sel_flags),
+                 (joint.row_of, per.row_of)):
+        assert np.array_equal(a, b)
+
+
+def test_per_level_differs_from_joint():
+    # N = 4, p = 2, L = 3, k_s = 2: quotas [1, 1].  Tokens 0 and 2 carry the
+    # largest norm 3, so both level-1 entries inherit 3 too; the joint
+    # ranking breaks the four-way tie by flat index and takes the two
+    # tokens, while the per-level quotas take one token and one level-1
+    # entry.  Flat layout: tokens 0-3, level-1 entries 4-5, root 6.
+    g = orc.Geometry(4, 2, 3, 2).check()
+    assert orc.level_quotas(g) == [1, 1]
+    Q = np.array([[3.0], [1.0], [3.0], [1.0]])
+    s = orc.sigma(*orc.scores(Q, np.zeros((4, 1)), g))
+    assert list(s) == [3.0, 1.0, 3.0, 1.0, 3.0, 3.0, 3.0]
+    assert list(orc.select(s, g).sel_idx) == [0, 2, 6]
+    assert list(orc.select(s, g, strata="per_level").sel_idx) == [0, 4, 6]
+    with pytest.raises(ValueError):
+        orc.select(s, g, strata="per_cell")
+
+
 @pytest.mark.parametrize("N,p,L,ks", [(256, 2, 4, 9), (512, 4, 4, 40), (512, 8, 3, 50)])
 def test_redundancy_is_token_coverage(N, p, L, ks):
     """Recursive rule == 'every token of the span is covered by a selected
