@@ -99,7 +99,8 @@ typedef int32_t lh_status;
 #define LH_STRATA_JOINT     0   /* one ranking over levels 0..L-2, the default */
 #define LH_STRATA_PER_LEVEL 1   /* a quota per level, ranked within the level:
                                    levels L-2 down to 1 in turn take
-                                   min(level size, remaining / levels left),
+                                   min(their entries in the stratum,
+                                   remaining / levels left),
                                    level 0 takes the rest (lh_validate
                                    rejects a budget where that would not fit
                                    in level 0; none with k_s <= T-1 was found
