@@ -6,7 +6,9 @@ Checked against the CPU oracle:
     bit-exact on every head (heads 0-1 of the 1M-token workload);
   * O, dQ, dK, dV of one sampled head within the stated tolerance
     (2e-2 + half a bf16 step of the reference, outputs being bf16);
-  * two runs byte-identical.
+  * two runs byte-identical;
+  * the per-level strata option's selection bit-exact on every head of the
+    530M-shape and 128K workloads.
 """
 import numpy as np
 import pytest
@@ -70,6 +72,31 @@ def test_fullsize_layer(wid):
         print(f"[full] {w.name} head {h} {n}: max|err| {err.max():.3e}, "
               f"max|ref| {np.abs(want).max():.2f}", flush=True)
         assert np.all(err <= tol), f"{n}: exceeds tolerance by {float(np.max(err - tol)):.3e}"
+
+
+@pytest.mark.parametrize("wid", [3, 4], ids=lambda i: synth.WORKLOADS[i].name.split()[0])
+def test_fullsize_per_level_selection(wid):
+    """The per-level strata option (reading R-7') at full size: the whole
+    selection from the GPU's score planes bit-exact against the oracle's on
+    every head."""
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[wid]
+    Q, K, V, _ = synth.make_inputs(w)
+    Qd, Kd, Vd = (x.to(dev) for x in (Q, K, V))
+    c = ops.Ctx(ops.make_dims(Qd, w.p, w.L, w.S, out_dtype=torch.bfloat16,
+                              strata_mode="per_level"))
+    _, _, _, sq, sk = ops.pyramid_score(c, Qd, Kd, Vd)
+    got = ops.topk_select(c, sq, sk)
+    torch.cuda.synchronize()
+    g = orc.Geometry(w.N, w.p, w.L, w.K).check()
+    for h in range(w.H):
+        sel = orc.select(orc.sigma(sq[0, h].cpu().numpy(), sk[0, h].cpu().numpy()), g,
+                         strata="per_level")
+        for t, want, name in zip(got, (sel.sel_idx, sel.sel_anchor, sel.sel_flags, sel.row_of),
+                                 ("sel_idx", "sel_anchor", "sel_flags", "row_of")):
+            assert np.array_equal(t[0, h].cpu().numpy(), want), f"{name} head {h}"
+    print(f"[full] {w.name}: per-level selection bit-exact on {w.H} heads", flush=True)
 
 
 def test_dense_one_level_at_full_length():
