@@ -14,8 +14,12 @@ comparison point (torch's fused SDPA, and this library's own MFMA kernels
 run as the one-level layer), and the CPU oracle timed on a bounded sample of
 the same workload.
 
+The step time is the median of the K timed steps (events between
+consecutive steps).  With the default (128K-token) workload the line also
+carries the step times of the other three large workloads ("workloads").
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 4]
-                       [--no-cpu] [--no-stages] [--no-dense]
+                       [--no-cpu] [--no-stages] [--no-dense] [--no-workloads]
 """
 from __future__ import annotations
 
@@ -48,6 +52,8 @@ def parse():
                     help="skip the dense causal attention comparisons, torch SDPA and this "
                          "library's kernels at L=1 (a few seconds at the 128K workload)")
     ap.add_argument("--stage-reps", type=int, default=10)
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the step timings of the other three large workloads")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache timings (L2 and Infinity Cache evicted before each rep)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -109,21 +115,45 @@ def counters_for(kernel: str, workload_name: str):
 
 def cpu_baseline(w, Q, K, V, dO):
     """The oracle as it stands, on head 0 of the workload: forward and
-    backward of one head, timed on this host; scaled to all heads."""
+    backward of one head, each stage timed on this host, the total rate
+    scaled to all heads.  The stages are the oracle's own functions, called
+    in the order of its head_forward / head_backward."""
     import threadpoolctl
     from oracle import lighthouse as orc
 
     g = orc.Geometry(w.N, w.p, w.L, w.K).check()
     q, k, v, do = (x[0, 0].double().numpy() for x in (Q, K, V, dO))
-    t0 = time.perf_counter()
-    fw = orc.head_forward(q, k, v, g, store="bf16" if w.dtype == "bf16" else None)
-    orc.head_backward(fw, do)
-    dt = time.perf_counter() - t0
+    store = "bf16" if w.dtype == "bf16" else None
+    t = {}
+
+    def timed(name, fn):
+        t0 = time.perf_counter()
+        r = fn()
+        t[name] = t.get(name, 0.0) + time.perf_counter() - t0
+        return r
+
+    scale = 1.0 / np.sqrt(w.d)
+    sQ, sK = timed("score", lambda: orc.scores(q, k, g))
+    sel = timed("topk_select", lambda: orc.select(orc.sigma(sQ, sK), g))
+    lv = timed("pyramid", lambda: [orc.pyramid(x, g, store) for x in (q, k, v)])
+    QS, KS, VS = timed("gather", lambda: [orc.gather(x, sel.sel_idx) for x in lv])
+    OS, LSE = timed("attn_fwd", lambda: orc.attention_fwd(QS, KS, VS, sel.sel_flags, scale))
+    timed("scatter", lambda: orc.scatter(OS, sel, g.N))
+    dOS = timed("scatter_bwd", lambda: orc.scatter_adjoint(do, sel, g.N))
+    dXS = timed("attn_bwd", lambda: orc.attention_bwd(QS, KS, VS, sel.sel_flags, scale, dOS))
+    timed("gather_bwd", lambda: [orc.pool_adjoint(orc.gather_adjoint(x, sel, g), g)
+                                 for x in dXS])
+    dt = sum(t.values())
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
     return {"value": w.N / (dt * w.H), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"head 0 of {w.H}, forward+backward of one head in {dt:.2f} s "
-                      f"(NumPy float64), rate scaled to all {w.H} heads"}
+                      f"(NumPy float64), rate scaled to all {w.H} heads",
+            "stage_s": {n: round(x, 4) for n, x in t.items()},
+            "near_ties": {"strata_near_tied": int(sel.near_tie.sum()), "strata": int(g.n_c),
+                          "head": 0, "rel": 1e-6,
+                          "what": "strata whose last selected and first unselected score "
+                                  "differ by at most 1e-6 of the stratum's largest score"}}
 
 
 def measured_peaks(torch, dev):
@@ -222,6 +252,50 @@ def dense_own(torch, ops, Q, K, V, dO, reps=2):
     return e0.elapsed_time(e1) / reps, o
 
 
+def time_steps(torch, step, warmup, steps):
+    """W untimed steps, then K steps back to back with an event between
+    consecutive steps (all on the current stream), bracketed by
+    synchronisations.  Returns (median, mean) ms per step."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return float(np.median(per)), ev[0].elapsed_time(ev[-1]) / steps
+
+
+def other_workload(torch, ops, synth, wid, warmup, steps):
+    """The layer step (lh_layer_fwd + lh_layer_bwd, bf16 in and out) on
+    another of the workloads, timed like the headline; inputs freed after."""
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[wid]
+    Qc, Kc, Vc, dOc = synth.make_inputs(w)
+    io = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    Q, K, V = (x.to(dev) for x in (Qc, Kc, Vc))
+    dO = dOc.to(dev, io)
+    del Qc, Kc, Vc, dOc
+    c = ops.Ctx(ops.make_dims(Q, w.p, w.L, w.S, out_dtype=io))
+    saved = ops.alloc_saved(c, dev)
+    o = torch.empty_like(Q, dtype=io)
+    ws = torch.empty(max(1, c.z.ws_layer_bwd), dtype=torch.uint8, device=dev)
+    grads = [torch.empty_like(Q, dtype=io) for _ in range(3)]
+
+    def step():
+        ops.layer_fwd(c, Q, K, V, saved=saved, o=o)
+        ops.layer_bwd(c, saved, dO, ws=ws, outs=grads)
+
+    ms, mean = time_steps(torch, step, warmup, steps)
+    del saved, o, ws, grads, Q, K, V, dO
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms_per_step": round(ms, 4), "ms_per_step_mean": round(mean, 4),
+            "tokens_per_s": round(w.B * w.N / (ms / 1e3), 1), "steps": steps, "warmup": warmup}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -262,18 +336,10 @@ def main():
               f"{args.copy_mib} MiB)", file=sys.stderr, flush=True)
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms, ms_mean = time_steps(torch, step, args.warmup, args.steps)
     value = w.B * w.N / (ms / 1e3)
-    print(f"[bench] layer fwd+bwd {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    print(f"[bench] layer fwd+bwd {ms:.3f} ms/step (median; mean {ms_mean:.3f})",
+          file=sys.stderr, flush=True)
 
     # cold caches: before each rep a 1 GiB write evicts the L2 and the
     # 256 MB Infinity Cache; events bracket the rep alone (the stream is in
@@ -393,6 +459,16 @@ def main():
         del do_, ref
         print(f"[bench] dense own {dense_mine}", file=sys.stderr, flush=True)
 
+    others = None
+    if not args.no_workloads and args.workload == 4:
+        del saved, ws, grads, o
+        torch.cuda.empty_cache()
+        others = {}
+        for wid in (2, 3, 5):
+            others[str(wid)] = other_workload(torch, ops, synth, wid, min(args.warmup, 3),
+                                              args.steps)
+            print(f"[bench] workload {others[str(wid)]}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, Qc, Kc, Vc, dOc.to(out))
@@ -400,12 +476,13 @@ def main():
     line = {
         "metric": "Lighthouse layer fwd+bwd tokens/sec at N=128K; per-stage HBM GB/s, MFMA util",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "ms_per_step_mean": round(ms_mean, 4),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "N": w.N, "H": w.H, "d": w.d, "p": w.p,
                    "L": w.L, "S": S, "K": w.K, "io_dtype": w.dtype, "out_dtype": w.dtype},
         "roofline": roof, "cpu_baseline": cpu, "measured_peaks": peaks, "cold": cold, "dense_sdpa": dense,
-        "dense_own_kernels": dense_mine, "stages": stages,
+        "dense_own_kernels": dense_mine, "stages": stages, "workloads": others,
     }
     print(json.dumps(line))
 

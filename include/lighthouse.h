@@ -39,8 +39,14 @@
  *    synchronises or reads device memory back to the host.
  *  - Outputs are overwritten, never accumulated.
  *  - Errors: every call validates its dims and pointers first and returns a
- *    negative lh_status without launching anything if they are invalid.  A
- *    failed launch returns LH_ERR_HIP.  No C++ exception crosses the ABI.
+ *    negative lh_status without launching anything if they are invalid.
+ *    lh_validate applies every limit a launch has (grid sizes, LDS budgets,
+ *    buffer-resource ranges), so a call whose dims it accepts is never
+ *    refused part-way.  A call that launches first clears any HIP error an
+ *    earlier call of the same host thread left pending, so that LH_ERR_HIP
+ *    reports a failure of its own launches.  After a fork onto the second
+ *    stream (below) the join back to `stream` is made on every return path,
+ *    error paths included.  No C++ exception crosses the ABI.
  *  - Concurrency: calls are reentrant; the library has no mutable global
  *    state apart from a per-device property cache and a per-device second
  *    stream with three events, each created once under a lock and kept until
@@ -117,7 +123,15 @@ typedef void *lh_stream;     /* a hipStream_t */
  *   out_dtype == LH_F32 when io_dtype == LH_F32, scale >= 0 and finite,
  *   scatter_mode in {LH_SCATTER_HOLD, LH_SCATTER_SPAN},
  *   sigma_mode in {LH_SIGMA_SUM, LH_SIGMA_MAX, LH_SIGMA_PRODUCT},
- *   strata_mode in {LH_STRATA_JOINT, LH_STRATA_PER_LEVEL}.
+ *   strata_mode in {LH_STRATA_JOINT, LH_STRATA_PER_LEVEL};
+ * and the launch limits of this build (LH_ERR_UNSUPPORTED otherwise):
+ *   B*H <= 65535, S < 2^31, T <= 7936 (one stratum's subtree in LDS), a
+ *   pyramid plan with B_c / p^g <= 256 / (d/8) rows for some g <= 6,
+ *   every grid's work-items along x within 2^32 - 1 (e.g. 64*B*H*S),
+ *   and for bf16 I/O: S*d*2 < 2^31 bytes per head (buffer-resource range)
+ *   and the forward's and the dQ kernel's LDS (their ring plus one REDUNDANT
+ *   bit per key, S/8 bytes) within 160 KiB, i.e. S up to about 490,000 at
+ *   d = 128.
  * The geometry (levels, strata, E, n_c, ...) is that of N rounded up to
  * whole coarsest cells of B_c = p^(L-1) tokens: n_c = ceil(N / B_c).  When N
  * is not a multiple of B_c (the pages assume whole cells; the reading taken
@@ -207,8 +221,9 @@ const char *lh_version(void);
 
 /* ---- stage 1: symmetric pyramid (explainer 2.A; news item: Theta(N)) ----
  * pq/pk/pv[b,h, off_l - N + i] = mean of the p children of entry (l-1, .),
- * i.e. the mean of tokens [i p^l, (i+1) p^l), for l = 1..L-1, accumulated in
- * float32 and rounded once to io_dtype.  Q, K and V are pooled alike.
+ * i.e. the mean of tokens [i p^l, (i+1) p^l), for l = 1..L-1: the block's
+ * tokens are summed in float64 (exact for bf16 and float32 inputs), divided
+ * by p^l and rounded once to io_dtype.  Q, K and V are pooled alike.
  * In: q, k, v [B,H,N,d] io_dtype.  Out: pq, pk, pv.  Any of the three pairs
  * may be skipped by passing NULL for both its input and output. */
 lh_status lh_pyramid_build(const lh_dims *dims, const void *q, const void *k,
@@ -376,9 +391,10 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *saved,
  * with no memory traffic.  Timing a launch gives the bf16 MFMA rate the
  * device sustains, the achievable ceiling beside the published peak.
  * out: device float32 [blocks * 256], caller-owned, overwritten with a
- * checksum.  Errors: LH_ERR_INVALID_ARG for blocks outside 1 .. 2^31-1,
- * iters <= 0 or a NULL out (nothing launched); LH_ERR_HIP after a failed
- * launch.  Asynchronous on `stream`. */
+ * checksum.  Errors: LH_ERR_INVALID_ARG for blocks outside 1 .. 2^24-1
+ * (the launch's work-items must fit 32 bits), iters <= 0 or a NULL out
+ * (nothing launched); LH_ERR_HIP after a failed launch.  Asynchronous on
+ * `stream`. */
 lh_status lh_probe_mfma_bf16(int64_t blocks, int32_t iters, float *out,
                              lh_stream stream);
 

@@ -384,18 +384,11 @@ def gather(levels, sel_idx):
 # --------------------------------------------------------------------------
 # O7  subsequence attention  [EXP-2C]
 # --------------------------------------------------------------------------
-def _allowed(flags):
-    """Allowed (query j, key j') pairs: j' <= j and key j' not redundant
-    (R-12; R-11 makes index order the span-causal order)."""
-    S = len(flags)
-    red = (np.asarray(flags) & FLAG_REDUNDANT) != 0
-    jj = np.arange(S)
-    return (jj[None, :] <= jj[:, None]) & (~red)[None, :]
-
-
 def attention_fwd(QS, KS, VS, flags, scale, row_block=2048):
-    """Standard scaled-dot-product attention on the subsequence with the mask
-    of _allowed (R-13: scale 1/sqrt(d) by default, no other bias).
+    """Standard scaled-dot-product attention on the subsequence.  Query j
+    sees key j' when j' <= j and row j' is not REDUNDANT (R-12; R-11 makes
+    index order the span-causal order).  R-13: scale 1/sqrt(d) by default,
+    no other bias.
     Returns OS [S, d] and LSE [S] (natural log of the softmax denominator of
     the scaled logits).  Rows are processed in chunks only to bound memory;
     each row's softmax is taken over its whole key set at once."""
@@ -655,15 +648,3 @@ def ragged_backward(fw: HeadForward, dO):
     N = np.asarray(dO).shape[0]
     dQ, dK, dV = head_backward(fw, _pad_rows(dO, fw.g.N))[:3]
     return dQ[:N], dK[:N], dV[:N]
-
-
-def layer_forward(Q, K_, V, p, L, K, scale=None, store=None, scatter_mode="hold",
-                  sigma_mode="sum", strata_mode="joint"):
-    """[B, H, N, d] arrays -> list over (b, h) of HeadForward."""
-    Q = np.asarray(Q)
-    B, H, N, _ = Q.shape
-    g = Geometry(N, p, L, K).check()
-    return [[head_forward(Q[b, h], K_[b, h], V[b, h], g, scale, store,
-                          scatter_mode=scatter_mode, sigma_mode=sigma_mode,
-                          strata_mode=strata_mode)
-             for h in range(H)] for b in range(B)]

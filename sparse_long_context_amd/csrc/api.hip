@@ -81,9 +81,17 @@ lh_status make_geo(const lh_dims *dm, Geo *g) {
   if (g->io == LH_F32 && g->out != LH_F32) return LH_ERR_UNSUPPORTED;
   g->Sp = (g->S + 63) / 64 * 64;
   g->scale = dm->scale == 0.0f ? (float)(1.0 / sqrt((double)g->d)) : dm->scale;
-  lh_status s = check_pyramid_supported(*g);
-  if (s != LH_OK) return s;
-  return check_select_supported(*g);
+  // every kernel family's launch limits, so that a call that passes
+  // validation launches nothing it would later have to refuse
+  lh_status (*const checks[])(const Geo &) = {
+      check_pyramid_supported, check_select_supported,    check_rows_supported,
+      check_attn_f32_supported, check_attn_fwd_supported, check_attn_dkv_supported,
+      check_attn_dq_supported};
+  for (auto chk : checks) {
+    const lh_status s = chk(*g);
+    if (s != LH_OK) return s;
+  }
+  return LH_OK;
 }
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -176,6 +184,28 @@ static lh_status side_stream(hipStream_t *s, hipEvent_t *fork, hipEvent_t *join,
   return LH_OK;
 }
 
+// Joins the side stream back to the caller's stream when it goes out of
+// scope (after a fork, on every return path): the side stream's work so far
+// is then complete whenever the caller's is, also when a launch on either
+// stream failed in between.  join() does it at a chosen point.
+struct SideJoin {
+  hipStream_t st, side;
+  hipEvent_t ev;
+  bool armed;
+  lh_status join() {
+    if (!armed) return LH_OK;
+    armed = false;
+    if (hipEventRecord(ev, side) != hipSuccess || hipStreamWaitEvent(st, ev, 0) != hipSuccess)
+      return LH_ERR_HIP;
+    return LH_OK;
+  }
+  ~SideJoin() { (void)join(); }
+};
+
+// Clears an error an earlier HIP call of this host thread left pending, so
+// that the status after this call's launches reports its own launches only.
+static void clear_pending_error() { (void)hipGetLastError(); }
+
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 static bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
 
@@ -253,6 +283,7 @@ lh_status lh_pyramid_build(const lh_dims *dims, const void *q, const void *k, co
     any += in[i] != nullptr;
   }
   LH_REQ(any > 0);
+  clear_pending_error();
   return launch_pyramid_score(g, q, k, v, pq, pk, pv, nullptr, nullptr, (hipStream_t)stream);
 }
 
@@ -262,6 +293,7 @@ lh_status lh_score(const lh_dims *dims, const void *q, const void *k, float *sq,
   LH_TRY(make_geo(dims, &g));
   LH_TRY(need_whole(g));
   LH_REQ(q && k && sq && sk && aligned16(q) && aligned16(k) && aligned4(sq) && aligned4(sk));
+  clear_pending_error();
   return launch_pyramid_score(g, q, k, nullptr, nullptr, nullptr, nullptr, sq, sk,
                               (hipStream_t)stream);
 }
@@ -276,6 +308,7 @@ lh_status lh_pyramid_score(const lh_dims *dims, const void *q, const void *k, co
   LH_REQ(g.L == 1 || (pq && pk && pv));
   LH_REQ(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(pq) && aligned16(pk) &&
          aligned16(pv) && aligned4(sq) && aligned4(sk));
+  clear_pending_error();
   return launch_pyramid_score(g, q, k, v, pq, pk, pv, sq, sk, (hipStream_t)stream);
 }
 
@@ -287,6 +320,7 @@ lh_status lh_topk_select(const lh_dims *dims, const float *sq, const float *sk,
   LH_REQ(sq && sk && sel_idx && sel_anchor && sel_flags && row_of);
   LH_REQ(aligned4(sq) && aligned4(sk) && aligned4(sel_idx) && aligned4(sel_anchor) &&
          aligned4(row_of));
+  clear_pending_error();
   return launch_select(g, sq, sk, sel_idx, sel_anchor, sel_flags, row_of, (hipStream_t)stream);
 }
 
@@ -317,6 +351,7 @@ lh_status lh_gather(const lh_dims *dims, const void *q, const void *k, const voi
          aligned16(pv) && aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned4(sel_idx));
   LH_REQ(aligned16(qst) && aligned16(kst) && aligned16(vst));
   if (g.io == LH_F32) LH_REQ(!qst && !kst && !vst);
+  clear_pending_error();
   return gather_impl(g, q, k, v, pq, pk, pv, sel_idx, qs, ks, vs, qst, kst, vst,
                      (hipStream_t)stream);
 }
@@ -329,6 +364,7 @@ lh_status lh_subseq_attn_fwd(const lh_dims *dims, const void *qs, const void *ks
   LH_REQ(qs && ks && vs && sel_flags && os && lse);
   LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(os) && aligned4(lse));
   hipStream_t st = (hipStream_t)stream;
+  clear_pending_error();
   if (g.io == LH_F32)
     return launch_attn_fwd_f32(g, (const float *)qs, (const float *)ks, (const float *)vs,
                                sel_flags, (float *)os, lse, st);
@@ -352,6 +388,7 @@ lh_status lh_subseq_attn_bwd(const lh_dims *dims, const void *qs, const void *ks
   hipStream_t st = (hipStream_t)stream;
   Carver c{(char *)ws, 0, ws_bytes};
   Sizes z = sizes_of(g);
+  clear_pending_error();
   if (g.io == LH_F32) {
     float *drow = (float *)c.take(z.drow);
     LH_TRY(launch_dos_prep(g, dos, (const float *)os, nullptr, nullptr, drow, st));
@@ -375,6 +412,7 @@ lh_status lh_attn_bwd_prep(const lh_dims *dims, const float *dos, const float *o
   LH_REQ(dos && os && dos_hi && dos_lo && drow);
   LH_REQ(aligned16(dos) && aligned16(os) && aligned16(dos_hi) && aligned16(dos_lo) &&
          aligned4(drow));
+  clear_pending_error();
   return launch_dos_prep(g, dos, os, (bf16_t *)dos_hi, (bf16_t *)dos_lo, drow,
                          (hipStream_t)stream);
 }
@@ -386,6 +424,7 @@ lh_status lh_attn_fwd_mfma(const lh_dims *dims, const void *qs, const void *ks, 
   if (g.io != LH_BF16) return LH_ERR_UNSUPPORTED;
   LH_REQ(qs && ks && vs && sel_flags && os && lse);
   LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(os) && aligned4(lse));
+  clear_pending_error();
   return launch_attn_fwd_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
                               sel_flags, os, lse, (hipStream_t)stream);
 }
@@ -401,6 +440,7 @@ lh_status lh_attn_bwd_dkv_mfma(const lh_dims *dims, const void *qs, const void *
   LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(dos_hi) &&
          aligned16(dos_lo) && aligned4(lse) && aligned4(drow) && aligned16(dks) &&
          aligned16(dvs));
+  clear_pending_error();
   return launch_attn_bwd_dkv_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
                                   (const bf16_t *)dos_hi, (const bf16_t *)dos_lo, lse, drow,
                                   sel_flags, dks, dvs, (hipStream_t)stream);
@@ -416,6 +456,7 @@ lh_status lh_attn_bwd_dq_mfma(const lh_dims *dims, const void *qs, const void *k
   LH_REQ(qs && ks && vs && dos_hi && dos_lo && lse && drow && sel_flags && dqs);
   LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(dos_hi) &&
          aligned16(dos_lo) && aligned4(lse) && aligned4(drow) && aligned16(dqs));
+  clear_pending_error();
   return launch_attn_bwd_dq_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
                                  (const bf16_t *)dos_hi, (const bf16_t *)dos_lo, lse, drow,
                                  sel_flags, dqs, (hipStream_t)stream);
@@ -428,6 +469,7 @@ lh_status lh_scatter(const lh_dims *dims, const void *os, const int32_t *sel_anc
   LH_TRY(need_whole(g));
   LH_REQ(os && sel_anchor && sel_flags && o);
   LH_REQ(aligned16(os) && aligned16(o) && aligned4(sel_anchor));
+  clear_pending_error();
   return launch_scatter(g, (const float *)os, sel_anchor, sel_flags, o, (hipStream_t)stream);
 }
 
@@ -438,6 +480,7 @@ lh_status lh_scatter_bwd(const lh_dims *dims, const void *dout, const int32_t *s
   LH_TRY(need_whole(g));
   LH_REQ(dout && sel_anchor && sel_flags && dos);
   LH_REQ(aligned16(dout) && aligned16(dos) && aligned4(sel_anchor));
+  clear_pending_error();
   return launch_scatter_bwd(g, dout, sel_anchor, sel_flags, dos, nullptr, nullptr, nullptr,
                             nullptr, (hipStream_t)stream);
 }
@@ -449,6 +492,7 @@ lh_status lh_span_owner(const lh_dims *dims, const int32_t *row_of, int32_t *own
   LH_TRY(need_whole(g));
   LH_REQ(row_of && owner);
   LH_REQ(aligned4(row_of) && aligned4(owner));
+  clear_pending_error();
   return launch_owner(g, row_of, owner, (hipStream_t)stream);
 }
 
@@ -459,6 +503,7 @@ lh_status lh_scatter_span(const lh_dims *dims, const float *os, const int32_t *o
   LH_TRY(need_whole(g));
   LH_REQ(os && owner && o);
   LH_REQ(aligned16(os) && aligned4(owner) && aligned16(o));
+  clear_pending_error();
   return launch_scatter_span(g, os, owner, o, (hipStream_t)stream);
 }
 
@@ -470,6 +515,7 @@ lh_status lh_scatter_span_bwd(const lh_dims *dims, const void *dout, const int32
   LH_TRY(need_whole(g));
   LH_REQ(dout && sel_idx && sel_flags && owner && dos);
   LH_REQ(aligned16(dout) && aligned4(sel_idx) && aligned4(owner) && aligned16(dos));
+  clear_pending_error();
   return launch_scatter_span_bwd(g, dout, sel_idx, sel_flags, owner, dos, nullptr, nullptr,
                                  nullptr, nullptr, (hipStream_t)stream);
 }
@@ -485,6 +531,7 @@ lh_status lh_gather_bwd(const lh_dims *dims, const float *dqs, const float *dks,
          aligned16(dq) && aligned16(dk) && aligned16(dv));
   const float *in[3] = {dqs, dks, dvs};
   void *out[3] = {dq, dk, dv};
+  clear_pending_error();
   return launch_unpool(g, in, row_of, out, 3, (hipStream_t)stream);
 }
 
@@ -511,6 +558,7 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
   const size_t need = ws_layer_fwd(g);
   if (need && (ws_bytes < need || !ws || !aligned16(ws))) return LH_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
+  clear_pending_error();
   Carver c{(char *)ws, 0, ws_bytes};
   int32_t *owner = g.mode == LH_SCATTER_SPAN ? (int32_t *)c.take(owner_bytes(g)) : nullptr;
   void *o_run = o;
@@ -540,6 +588,7 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
     LH_TRY(side_stream(&side, &fork, &join, &mid));
     if (hipEventRecord(fork, st) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess)
       return LH_ERR_HIP;
+    SideJoin sj{st, side, join, true};
     LH_TRY(launch_pyramid_score(g, nullptr, nullptr, v, nullptr, nullptr, s->pv, nullptr, nullptr,
                                 side));
     LH_TRY(launch_select(g, s->sq, s->sk, s->sel_idx, s->sel_anchor, s->sel_flags, s->row_of,
@@ -549,9 +598,8 @@ lh_status lh_layer_fwd(const lh_dims *dims, const void *q, const void *k, const 
     const void *src[3] = {q, k, v}, *psrc[3] = {s->pq, s->pk, s->pv};
     void *dst[3] = {s->qs, s->ks, s->vs};
     LH_TRY(launch_gather(g, src, psrc, s->sel_idx, dst, side, 2, 1));
-    if (hipEventRecord(join, side) != hipSuccess) return LH_ERR_HIP;
     LH_TRY(launch_gather(g, src, psrc, s->sel_idx, dst, st, 0, 2));
-    if (hipStreamWaitEvent(st, join, 0) != hipSuccess) return LH_ERR_HIP;
+    LH_TRY(sj.join());
   }
   const bool bf = g.io == LH_BF16;
   // bf16 I/O in hold mode: the attention kernel also writes the output
@@ -585,6 +633,7 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
   const size_t need = ws_layer_bwd(g);
   if (ws_bytes < need || !ws || !aligned16(ws)) return LH_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
+  clear_pending_error();
   Sizes z = sizes_of(g);
   Carver c{(char *)ws, 0, ws_bytes};
   float *dqs = (float *)c.take(z.subseq_f32);
@@ -629,17 +678,17 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
     LH_TRY(side_stream(&side, &fork, &join));
     if (hipEventRecord(fork, st) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess)
       return LH_ERR_HIP;
+    SideJoin sj{st, side, join, true};
     const float *in_kv[2] = {dks, dvs};
     void *out_kv[2] = {grad[1], grad[2]};
     LH_TRY(launch_unpool(g, in_kv, s->row_of, out_kv, 2, side));
-    if (hipEventRecord(join, side) != hipSuccess) return LH_ERR_HIP;
     LH_TRY(launch_attn_bwd_dq_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
                                    (const bf16_t *)s->vs, dhi, dlo, s->lse, drow, s->sel_flags,
                                    dqs, st));
     const float *in_q[1] = {dqs};
     void *out_q[1] = {grad[0]};
     LH_TRY(launch_unpool(g, in_q, s->row_of, out_q, 1, st));
-    if (hipStreamWaitEvent(st, join, 0) != hipSuccess) return LH_ERR_HIP;
+    LH_TRY(sj.join());
   } else {
     float *dos = (float *)c.take(z.subseq_f32);
     if (!c.ok()) return LH_ERR_WORKSPACE;

@@ -381,11 +381,20 @@ void attn_bwd_dkv_kernel(
     }
 }
 
+// bf16 I/O: one head's rows fit a buffer resource and the grid's
+// work-items fit 32 bits (the ring's LDS does not depend on the geometry)
+lh_status check_attn_dkv_supported(const Geo &g) {
+  static_assert(sizeof(KvStage<128>) * kKvStages <= kMaxLds, "the d = 128 ring fits");
+  if (g.io != LH_BF16) return LH_OK;
+  if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
+  return grid_fits((int64_t)cdiv(g.S, kKvBK) * g.BH(), kKvThreads) ? LH_OK : LH_ERR_UNSUPPORTED;
+}
+
 lh_status launch_attn_bwd_dkv_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                    const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
                                    const float *lse, const float *drow, const uint8_t *flags,
                                    float *dks, float *dvs, hipStream_t st) {
-  if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
+  if (check_attn_dkv_supported(g) != LH_OK) return LH_ERR_UNSUPPORTED;
   const unsigned items = cdiv(g.S, kKvBK) * (unsigned)g.BH();
 #define LH_DKV(D)                                                                             \
   do {                                                                                        \

@@ -324,18 +324,31 @@ void attn_bwd_dq_kernel(
 }
 
 
+// LDS of one dQ workgroup: the ring, then one REDUNDANT bit per key of the
+// widest key range
+static size_t dq_lds(const Geo &g) {
+  const size_t ring = g.d == 128 ? sizeof(QStage<128>) * kQStages : sizeof(QStage<64>) * kQStages;
+  return ring + (size_t)((g.S + 63) / 64 * 8);
+}
+
+// bf16 I/O: one head's rows fit a buffer resource, the grid's work-items
+// fit 32 bits, and the LDS fits
+lh_status check_attn_dq_supported(const Geo &g) {
+  if (g.io != LH_BF16) return LH_OK;
+  if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
+  if (!grid_fits((int64_t)cdiv(g.S, kQBQ) * g.BH(), kQThreads)) return LH_ERR_UNSUPPORTED;
+  return dq_lds(g) <= kMaxLds ? LH_OK : LH_ERR_UNSUPPORTED;
+}
+
 lh_status launch_attn_bwd_dq_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                   const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
                                   const float *lse, const float *drow, const uint8_t *flags,
                                   float *dqs, hipStream_t st) {
-  if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
+  if (check_attn_dq_supported(g) != LH_OK) return LH_ERR_UNSUPPORTED;
   const unsigned items = cdiv(g.S, kQBQ) * (unsigned)g.BH();
-  // LDS: the ring, then one REDUNDANT bit per key of the widest key range
-  const size_t flb = (size_t)((g.S + 63) / 64 * 8);
+  const size_t shm = dq_lds(g);
 #define LH_DQ(D)                                                                              \
   do {                                                                                        \
-    const size_t shm = sizeof(QStage<D>) * kQStages + flb;                                    \
-    if (shm > kMaxLds) return LH_ERR_UNSUPPORTED;                                             \
     (void)hipFuncSetAttribute((const void *)attn_bwd_dq_kernel<D>,                            \
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);          \
     hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(items), dim3(kQThreads), shm, st, qs, ks,  \

@@ -183,6 +183,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_f32_kernel(
   }
 }
 
+// one workgroup of 256 per 4 rows of every head along x
+lh_status check_attn_f32_supported(const Geo &g) {
+  return grid_fits(cdiv(g.S, 4), 256) ? LH_OK : LH_ERR_UNSUPPORTED;
+}
+
 lh_status launch_attn_fwd_f32(const Geo &g, const float *qs, const float *ks, const float *vs,
                               const uint8_t *flags, float *os, float *lse, hipStream_t st) {
   dim3 grid(cdiv(g.S, 4), (unsigned)g.BH());

@@ -385,27 +385,41 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
                                                wg, col, h, tid, bh, otok, N);
 }
 
+// LDS of one forward workgroup: the ring, then one REDUNDANT bit per key of
+// the widest key range, then (output scatter) the workgroup's anchors,
+// leaders and two bounds.  The merge reuses the ring (256 lanes x (16 DB +
+// 2) floats), and so do the staged output rows.
+static size_t fwd_lds(const Geo &g, bool epi) {
+  const size_t ring = g.d == 128 ? sizeof(KeyStage<128>) * 2 * kFwdPairs
+                                 : sizeof(KeyStage<64>) * 2 * kFwdPairs;
+  const size_t flb = (size_t)((g.S + 63) / 64 * 8);
+  const size_t epb = epi ? (2 * kFwdBQ + 2) * sizeof(int32_t) : 0;
+  return ring + flb + epb;
+}
+
+// bf16 I/O: one head's rows fit a buffer resource, the grid's work-items
+// fit 32 bits, and the LDS of the output-writing form (the larger) fits
+lh_status check_attn_fwd_supported(const Geo &g) {
+  if (g.io != LH_BF16) return LH_OK;
+  if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
+  if (!grid_fits((int64_t)cdiv(g.S, kFwdBQ) * g.BH(), kFwdThreads)) return LH_ERR_UNSUPPORTED;
+  return fwd_lds(g, true) <= kMaxLds ? LH_OK : LH_ERR_UNSUPPORTED;
+}
+
 lh_status launch_attn_fwd_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                const bf16_t *vs, const uint8_t *flags, float *os, float *lse,
                                hipStream_t st, const int32_t *sel_anchor, void *o) {
-  if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
+  if (check_attn_fwd_supported(g) != LH_OK) return LH_ERR_UNSUPPORTED;
   const unsigned items = cdiv(g.S, kFwdBQ) * (unsigned)g.BH();
   const float sl2 = g.scale * 1.4426950408889634f;
-  // LDS: the ring, then one REDUNDANT bit per key of the widest key range,
-  // then (output scatter) the workgroup's anchors, leaders and two bounds.
-  // The merge reuses the ring (256 lanes x (16 DB + 2) floats), and so do
-  // the staged output rows.
-  const size_t flb = (size_t)((g.S + 63) / 64 * 8);
   const int epi = o ? (g.out == LH_BF16 ? 1 : 2) : 0;
-  const size_t epb = o ? (2 * kFwdBQ + 2) * sizeof(int32_t) : 0;
 #define LH_FWD(D, E)                                                                          \
   do {                                                                                        \
     static_assert(sizeof(KeyStage<D>) * 2 * kFwdPairs >= 256 * (16 * (D / 32) + 2) * 4,       \
                   "the merge fits in the ring");                                              \
     static_assert(sizeof(KeyStage<D>) * 2 * kFwdPairs >= kFwdBQ * D * 4,                      \
                   "the staged output rows fit in the ring");                                  \
-    const size_t shm = sizeof(KeyStage<D>) * 2 * kFwdPairs + flb + epb;                       \
-    if (shm > kMaxLds) return LH_ERR_UNSUPPORTED;                                             \
+    const size_t shm = fwd_lds(g, E != 0);                                                    \
     (void)hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel<D, E>,                       \
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);          \
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, E>), dim3(items), dim3(kFwdThreads), shm, st, \

@@ -36,7 +36,9 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(float *out, i
 
 extern "C" lh_status lh_probe_mfma_bf16(int64_t blocks, int32_t iters, float *out,
                                         lh_stream stream) {
-  if (blocks <= 0 || blocks > 0x7fffffff || iters <= 0 || !out) return LH_ERR_INVALID_ARG;
+  if (!lh::grid_fits(blocks, lh::kProbeThreads) || blocks <= 0 || iters <= 0 || !out)
+    return LH_ERR_INVALID_ARG;
+  (void)hipGetLastError();   // report this launch's error only
   hipLaunchKernelGGL(lh::mfma_probe_kernel, dim3((unsigned)blocks), dim3(lh::kProbeThreads), 0,
                      (hipStream_t)stream, out, iters);
   return lh::hip_status();

@@ -732,6 +732,26 @@ static int unpool_spw(const Geo &g) {
   return spw;
 }
 
+// every launch of this file fits its grid limits for the geometry (grid x in
+// work-items within 32 bits; y = B*H and z <= 3 are checked by make_geo) and
+// the unpool kernel's LDS staging holds one stratum's row_of entries
+lh_status check_rows_supported(const Geo &g) {
+  const int64_t S = g.S, N = g.N, BH = g.BH();
+  const int cpr = g.d / 8;
+  const int64_t row_vec = (int64_t)g.d * 4 / 16;   // widest token row (float32) in 16 B
+  const bool ok = grid_fits(cdiv(S, 256 / cpr), 256) &&            // gather
+                  grid_fits(g.Sp / 64, 256) &&                      // transpose
+                  grid_fits(g.n_c * (int64_t)cdiv(g.Bc, kScatChunk), 256) &&   // scatter
+                  grid_fits(cdiv(S, 4), 256) &&                     // scatter adjoints
+                  grid_fits(cdiv(N * row_vec, 256), 256) &&         // copy_rows
+                  grid_fits(cdiv(N, 256), 256) &&                   // owner
+                  grid_fits(cdiv(N, (256 / cpr) * 8), 256) &&       // span scatter
+                  grid_fits(cdiv(BH * S, 4), 256) &&                // dos_prep (all heads)
+                  grid_fits(g.n_c, kUnpoolThreads);                  // unpool
+  if (!ok) return LH_ERR_UNSUPPORTED;
+  return g.T <= kUnpoolLdsEntries ? LH_OK : LH_ERR_UNSUPPORTED;
+}
+
 lh_status launch_unpool(const Geo &g, const float *const dxs[], const int32_t *row_of,
                         void *const dx[], int nt, hipStream_t st) {
   if (g.T > kUnpoolLdsEntries) return LH_ERR_UNSUPPORTED;

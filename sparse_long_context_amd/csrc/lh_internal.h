@@ -120,6 +120,14 @@ lh_status launch_select(const Geo &g, const float *sq, const float *sk, int32_t 
                         int32_t *sel_anchor, uint8_t *sel_flags, int32_t *row_of,
                         hipStream_t st);
 lh_status check_select_supported(const Geo &g);
+// launch limits of the other kernel families (grid sizes, LDS budgets,
+// buffer-resource ranges), so that lh_validate rejects every geometry a
+// launch would reject
+lh_status check_rows_supported(const Geo &g);
+lh_status check_attn_f32_supported(const Geo &g);
+lh_status check_attn_fwd_supported(const Geo &g);
+lh_status check_attn_dkv_supported(const Geo &g);
+lh_status check_attn_dq_supported(const Geo &g);
 
 // tensors z0 .. z0 + nz - 1 of the three (0 q, 1 k, 2 v)
 lh_status launch_gather(const Geo &g, const void *const src[3], const void *const psrc[3],
@@ -186,5 +194,11 @@ inline lh_status hip_status() {
 }
 
 inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+// a one-dimensional launch of `blocks` workgroups of `threads` work-items:
+// the work-item count along x must fit 32 bits
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+  return blocks >= 0 && blocks <= (int64_t)UINT32_MAX / threads;
+}
 
 }  // namespace lh

@@ -25,6 +25,8 @@ Recipe (per workload c = 1..5):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -110,18 +112,25 @@ def head_tensor(w: Workload, tensor_id: int, h: int, mult=None, seed=None):
 
 def make_inputs(w: Workload, heads=None, seed=None):
     """Q, K, V, dO as CPU torch tensors [B, len(heads), N, d] in the
-    workload dtype (B = 1)."""
+    workload dtype (B = 1).  Every (tensor, head) has its own generator, so
+    they are drawn in parallel threads; the values do not depend on the
+    thread count."""
     seed = SEED_BASE + w.cid if seed is None else seed
     heads = list(range(w.H)) if heads is None else list(heads)
     mults = _row_multipliers(w, seed, heads)
     tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-    out = []
-    for tid in range(4):
-        t = torch.empty((1, len(heads), w.N, w.d), dtype=tdt)
-        for k, h in enumerate(heads):
-            x = head_tensor(w, tid, h, None if mults is None else mults[h], seed)
-            t[0, k] = torch.from_numpy(x).to(tdt)
-        out.append(t)
+    out = [torch.empty((1, len(heads), w.N, w.d), dtype=tdt) for _ in range(4)]
+
+    def fill(job):
+        tid, k = job
+        h = heads[k]
+        x = head_tensor(w, tid, h, None if mults is None else mults[h], seed)
+        out[tid][0, k] = torch.from_numpy(x).to(tdt)
+
+    jobs = [(tid, k) for tid in range(4) for k in range(len(heads))]
+    workers = max(1, min(16, os.cpu_count() or 1, len(jobs)))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, jobs))
     return tuple(out)
 
 

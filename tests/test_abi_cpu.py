@@ -206,3 +206,43 @@ def test_mfma_probe_rejects_bad_args_without_launch(lib):
                                (8, 10, None)):
         st = lib.lh_probe_mfma_bf16(blocks, iters, out, None)
         assert st == L.LH_ERR_INVALID_ARG, (blocks, iters, out, st)
+
+
+@pytest.mark.parametrize("d,S", [(128, 524288), (128, 1048576), (64, 1048576)])
+def test_validate_rejects_what_the_attention_kernels_cannot_launch(lib, d, S):
+    """L = 1 (dense, S = N) with bf16 I/O: the forward and dQ kernels keep one
+    REDUNDANT bit per key in LDS beside their rings, so past about 490,000
+    keys at d = 128 (more at d = 64) they do not fit; lh_validate must say so,
+    and the layer calls must return the same code before launching anything
+    (every pointer below is a fake address that is never dereferenced)."""
+    dd = dims(N=S, H=1, d=d, p=2, L=1, K=0, S=S, io_dtype=L.LH_BF16, out_dtype=L.LH_BF16)
+    assert lib.lh_validate(C.byref(dd)) == L.LH_ERR_UNSUPPORTED
+    p = C.c_void_p(0x10000)
+    s = L.Saved(*([0x10000] * 17))
+    assert lib.lh_layer_fwd(C.byref(dd), p, p, p, p, C.byref(s), None, 0, None) == \
+        L.LH_ERR_UNSUPPORTED
+    assert lib.lh_layer_bwd(C.byref(dd), C.byref(s), p, p, p, p, p, 1 << 40, None) == \
+        L.LH_ERR_UNSUPPORTED
+    assert lib.lh_attn_fwd_mfma(C.byref(dd), p, p, p, p, p, p, None) == L.LH_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(N=262144, H=1, d=128, p=2, L=1, K=0, S=262144),   # forward and dQ LDS fit
+    dict(N=131072, H=8, d=128, p=4, L=6, K=8064, S=8192),  # the 128K workload
+    dict(N=1048576, H=4, d=128, p=8, L=5, K=16128, S=16384),
+])
+def test_validate_accepts_the_workload_shapes(lib, kw):
+    dd = dims(io_dtype=L.LH_BF16, out_dtype=L.LH_BF16, **kw)
+    assert lib.lh_validate(C.byref(dd)) == L.LH_OK
+
+
+def test_validate_rejects_grids_past_32_bits(lib):
+    """64 work-items per subsequence row of every head in one dimension (the
+    dO split of the attention backward) must fit 32 bits."""
+    dd = dims(B=1, N=2 ** 20, H=1024, d=64, p=4, L=3, K=3 * 2 ** 16, S=2 ** 18,
+              io_dtype=L.LH_BF16, out_dtype=L.LH_BF16)
+    assert lib.lh_validate(C.byref(dd)) == L.LH_ERR_UNSUPPORTED
+    dd.H = 256   # 64 * 256 * 2^18 = 2^32: one past the limit
+    assert lib.lh_validate(C.byref(dd)) == L.LH_ERR_UNSUPPORTED
+    dd.H = 128
+    assert lib.lh_validate(C.byref(dd)) == L.LH_OK
