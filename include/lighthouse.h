@@ -294,6 +294,27 @@ lh_status lh_subseq_attn_bwd(const lh_dims *dims, const void *qs,
                              float *dvs, void *ws, size_t ws_bytes,
                              lh_stream stream);
 
+/* ---- stage 3b backward without a workspace argument ----
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The same
+ * operation, arguments and kernels as lh_subseq_attn_bwd, but the scratch
+ * it needs (the dO split and drow, sizes.ws_attn_bwd bytes) lives in a
+ * fixed device array inside the library, LH_NOALLOC_SCRATCH_BYTES per
+ * device, held from the library's first use on a device until the process
+ * ends.  Nothing is allocated or freed by the call.  Every call on one
+ * device shares that device's array (no part of it needs to start at zero:
+ * each call overwrites what it reads), so calls that overlap in time on one
+ * device race and must be ordered by the caller (e.g. one stream).
+ * Errors: as lh_subseq_attn_bwd, and LH_ERR_UNSUPPORTED when
+ * sizes.ws_attn_bwd exceeds LH_NOALLOC_SCRATCH_BYTES (nothing launched). */
+#define LH_NOALLOC_SCRATCH_BYTES (80u << 20)
+lh_status lh_subseq_attn_bwd_noalloc(const lh_dims *dims, const void *qs,
+                                     const void *ks, const void *vs,
+                                     const void *os, const float *lse,
+                                     const uint8_t *sel_flags, const float *dos,
+                                     float *dqs, float *dks, float *dvs,
+                                     lh_stream stream);
+
 /* ---- stage 3b, operand-prepared forms: each of the three MFMA calls
  * launches exactly one kernel (LH_BF16 I/O only; LH_ERR_UNSUPPORTED
  * otherwise).  They take the operand layouts the kernels read directly, for

@@ -19,6 +19,7 @@ LH_ROW_REDUNDANT, LH_ROW_LEADER = 1, 2
 LH_SCATTER_HOLD, LH_SCATTER_SPAN = 0, 1
 LH_SIGMA_SUM, LH_SIGMA_MAX, LH_SIGMA_PRODUCT = 0, 1, 2
 LH_STRATA_JOINT, LH_STRATA_PER_LEVEL = 0, 1
+LH_NOALLOC_SCRATCH_BYTES = 80 << 20
 
 
 class LighthouseError(RuntimeError):
@@ -61,6 +62,7 @@ _PROTOS = {
     "lh_gather": [_P] * 13 + [_P],
     "lh_subseq_attn_fwd": [_P] * 6 + [_P, C.c_size_t, _P],
     "lh_subseq_attn_bwd": [_P] * 10 + [_P, C.c_size_t, _P],
+    "lh_subseq_attn_bwd_noalloc": [_P] * 10 + [_P],
     "lh_attn_bwd_prep": [_P] * 5 + [_P],
     "lh_attn_fwd_mfma": [_P] * 6 + [_P],
     "lh_attn_bwd_dkv_mfma": [_P] * 10 + [_P],

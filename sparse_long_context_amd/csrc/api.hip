@@ -374,18 +374,12 @@ lh_status lh_subseq_attn_fwd(const lh_dims *dims, const void *qs, const void *ks
                               sel_flags, (float *)os, lse, st);
 }
 
-lh_status lh_subseq_attn_bwd(const lh_dims *dims, const void *qs, const void *ks,
-                             const void *vs, const void *os, const float *lse,
-                             const uint8_t *sel_flags, const float *dos, float *dqs, float *dks,
-                             float *dvs, void *ws, size_t ws_bytes, lh_stream stream) {
-  Geo g;
-  LH_TRY(make_geo(dims, &g));
-  LH_REQ(qs && ks && vs && os && lse && sel_flags && dos && dqs && dks && dvs);
-  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(os) && aligned4(lse) &&
-         aligned16(dos) && aligned16(dqs) && aligned16(dks) && aligned16(dvs));
-  const size_t need = ws_attn_bwd(g);
-  if (ws_bytes < need || !ws || !aligned16(ws)) return LH_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+// the attention backward after validation: the dO split and drow go to the
+// workspace `ws` of at least ws_attn_bwd(g) bytes
+static lh_status attn_bwd_impl(const Geo &g, const void *qs, const void *ks, const void *vs,
+                               const void *os, const float *lse, const uint8_t *sel_flags,
+                               const float *dos, float *dqs, float *dks, float *dvs, void *ws,
+                               size_t ws_bytes, hipStream_t st) {
   Carver c{(char *)ws, 0, ws_bytes};
   Sizes z = sizes_of(g);
   clear_pending_error();
@@ -402,6 +396,74 @@ lh_status lh_subseq_attn_bwd(const lh_dims *dims, const void *qs, const void *ks
   LH_TRY(launch_dos_prep(g, dos, (const float *)os, dhi, dlo, drow, st));
   return launch_attn_bwd_bf16(g, (const bf16_t *)qs, (const bf16_t *)ks, (const bf16_t *)vs,
                               dhi, dlo, lse, drow, sel_flags, dqs, dks, dvs, st);
+}
+
+static lh_status attn_bwd_args(const Geo &g, const void *qs, const void *ks, const void *vs,
+                               const void *os, const float *lse, const uint8_t *sel_flags,
+                               const float *dos, const float *dqs, const float *dks,
+                               const float *dvs) {
+  (void)g;
+  LH_REQ(qs && ks && vs && os && lse && sel_flags && dos && dqs && dks && dvs);
+  LH_REQ(aligned16(qs) && aligned16(ks) && aligned16(vs) && aligned16(os) && aligned4(lse) &&
+         aligned16(dos) && aligned16(dqs) && aligned16(dks) && aligned16(dvs));
+  return LH_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-alloc form
+// Scratch memory of lh_subseq_attn_bwd_noalloc: a fixed device array (each
+// device that loads the library holds its own copy until the process ends).
+// In host code `scratch` names a host-side stand-in, not device memory; the
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is handed to kernels.
+namespace lh {
+constexpr size_t kNoAllocScratch = (size_t)LH_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+static std::mutex g_scratch_mu;
+static void *g_scratch[kMaxDevices];
+
+static lh_status scratch_ptr(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LH_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LH_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return LH_OK;
+}
+}  // namespace lh
+
+extern "C" {
+
+lh_status lh_subseq_attn_bwd(const lh_dims *dims, const void *qs, const void *ks,
+                             const void *vs, const void *os, const float *lse,
+                             const uint8_t *sel_flags, const float *dos, float *dqs, float *dks,
+                             float *dvs, void *ws, size_t ws_bytes, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_TRY(attn_bwd_args(g, qs, ks, vs, os, lse, sel_flags, dos, dqs, dks, dvs));
+  if (ws_bytes < ws_attn_bwd(g) || !ws || !aligned16(ws)) return LH_ERR_WORKSPACE;
+  return attn_bwd_impl(g, qs, ks, vs, os, lse, sel_flags, dos, dqs, dks, dvs, ws, ws_bytes,
+                       (hipStream_t)stream);
+}
+
+lh_status lh_subseq_attn_bwd_noalloc(const lh_dims *dims, const void *qs, const void *ks,
+                                     const void *vs, const void *os, const float *lse,
+                                     const uint8_t *sel_flags, const float *dos, float *dqs,
+                                     float *dks, float *dvs, lh_stream stream) {
+  Geo g;
+  LH_TRY(make_geo(dims, &g));
+  LH_TRY(attn_bwd_args(g, qs, ks, vs, os, lse, sel_flags, dos, dqs, dks, dvs));
+  const size_t need = ws_attn_bwd(g);
+  if (need > kNoAllocScratch) return LH_ERR_UNSUPPORTED;
+  void *ws = nullptr;
+  LH_TRY(scratch_ptr(&ws));
+  return attn_bwd_impl(g, qs, ks, vs, os, lse, sel_flags, dos, dqs, dks, dvs, ws,
+                       kNoAllocScratch, (hipStream_t)stream);
 }
 
 lh_status lh_attn_bwd_prep(const lh_dims *dims, const float *dos, const float *os, void *dos_hi,

@@ -156,6 +156,22 @@ def subseq_attn_bwd(c: Ctx, qs, ks, vs, os_, lse, flags, dos):
     return dqs, dks, dvs
 
 
+def subseq_attn_bwd_noalloc(c: Ctx, qs, ks, vs, os_, lse, flags, dos, outs=None):
+    """lh_subseq_attn_bwd_noalloc: the same backward with the library's fixed
+    scratch array instead of a workspace (outputs may be passed in)."""
+    dev = qs.device
+    _need(dos, _bh(c) + (c.S, c.d), torch.float32, "dos")
+    _need(os_, _bh(c) + (c.S, c.d), torch.float32, "os")
+    if outs is None:
+        outs = [c.empty(*_bh(c), c.S, c.d, dtype=torch.float32, device=dev) for _ in range(3)]
+    for n, t in zip(("dqs", "dks", "dvs"), outs):
+        _need(t, _bh(c) + (c.S, c.d), torch.float32, n)
+    dqs, dks, dvs = outs
+    c.call("lh_subseq_attn_bwd_noalloc", _ptr(qs), _ptr(ks), _ptr(vs), _ptr(os_), _ptr(lse),
+           _ptr(flags), _ptr(dos), _ptr(dqs), _ptr(dks), _ptr(dvs), _stream())
+    return dqs, dks, dvs
+
+
 def attn_bwd_prep(c: Ctx, dos, os_):
     """Operands of the two backward MFMA kernels (bf16 I/O only): the
     two-term bf16 split of dOS and drow = rowsum(dOS * OS)."""
