@@ -177,6 +177,7 @@ def measured_peaks(torch, dev):
     torch.cuda.synchronize()
     copy_gbs = 2 * 4 * n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
     del a, b
+    stream = stream_probe(torch, dev, _lib, C, st)
     blocks, iters = 256 * 8, 2000
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     fn = _lib.lib().lh_probe_mfma_bf16
@@ -189,8 +190,36 @@ def measured_peaks(torch, dev):
     flops = blocks * 4 * 8 * iters * 32768.0
     mfma_tf = flops / (e0.elapsed_time(e1) / 1e3) / 1e12
     return {"hbm_copy_GBps": round(copy_gbs, 1), "mfma_bf16_TFLOPs": round(mfma_tf, 1),
-            "how": "one 1 GiB device copy (read+write); lh_probe_mfma_bf16, 2048 workgroups x "
-                   "2000 rounds of 8 independent 32x32x16 bf16 MFMAs per wavefront"}
+            "stream_GBps": stream,
+            "how": "one 1 GiB torch device copy (read+write); lh_probe_stream over 2 GiB (copy, "
+                   "read-only, write-only; best grid of several); lh_probe_mfma_bf16, 2048 "
+                   "workgroups x 2000 rounds of 8 independent 32x32x16 bf16 MFMAs per wavefront"}
+
+
+def stream_probe(torch, dev, _lib, C, st, nbytes=2 << 30):
+    """The library's streaming probe: best GB/s over a few grid sizes for a
+    copy (read + write bytes), a read-only and a write-only pass."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    fn = _lib.lib().lh_probe_stream
+    sp = C.c_void_p(st.cuda_stream)
+    out = {}
+    for mode, name, moved in ((0, "copy", 2 * nbytes), (1, "read", nbytes), (2, "write", nbytes)):
+        best = 0.0
+        for blocks in (2048, 4096, 8192, 16384):
+            _lib.check(fn(mode, C.c_void_p(src.data_ptr()), C.c_void_p(dst.data_ptr()), nbytes,
+                          blocks, sp), "lh_probe_stream")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(3):
+                _lib.check(fn(mode, C.c_void_p(src.data_ptr()), C.c_void_p(dst.data_ptr()),
+                              nbytes, blocks, sp), "lh_probe_stream")
+            e1.record(st)
+            torch.cuda.synchronize()
+            best = max(best, moved * 3 / (e0.elapsed_time(e1) / 1e3) / 1e9)
+        out[name] = round(best, 1)
+    del src, dst
+    return out
 
 
 def dense_sdpa(torch, Q, K, V, dO, reps=2):

@@ -419,6 +419,22 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *saved,
 lh_status lh_probe_mfma_bf16(int64_t blocks, int32_t iters, float *out,
                              lh_stream stream);
 
+/* ---- measurement helper (not part of the layer) ----
+ * Streams `bytes` bytes through HBM with 16-byte accesses, four in flight
+ * per lane, over `blocks` workgroups of 256 threads (grid-stride), so that
+ * timing a launch gives the bandwidth this device sustains for the kind of
+ * traffic the memory-bound stages make:
+ *   mode 0: copy src -> dst (reads and writes `bytes` each);
+ *   mode 1: read src only; dst receives one uint32 checksum per thread
+ *           (blocks * 256 * 4 bytes);
+ *   mode 2: write dst only (a fixed pattern).
+ * Pointers are device pointers, 16-byte aligned, caller-owned; bytes must be
+ * a positive multiple of 16.  Errors: LH_ERR_INVALID_ARG for a bad mode,
+ * size, pointer or blocks outside 1 .. 2^24-1 (nothing launched);
+ * LH_ERR_HIP after a failed launch.  Asynchronous on `stream`. */
+lh_status lh_probe_stream(int32_t mode, const void *src, void *dst, size_t bytes,
+                          int64_t blocks, lh_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -77,7 +77,7 @@ _PROTOS = {
     "lh_layer_bwd": [C.POINTER(Saved)] + [_P] * 4 + [_P, C.c_size_t, _P],
 }
 EXPORTS = ["lh_validate", "lh_get_sizes", "lh_status_string", "lh_version", "lh_probe_mfma_bf16",
-           *_PROTOS]
+           "lh_probe_stream", *_PROTOS]
 
 _lib = None
 _lock = threading.Lock()
@@ -102,6 +102,8 @@ def lib():
             L.lh_version.restype = C.c_char_p
             L.lh_probe_mfma_bf16.argtypes = [C.c_int64, C.c_int32, _P, _P]
             L.lh_probe_mfma_bf16.restype = C.c_int32
+            L.lh_probe_stream.argtypes = [C.c_int32, _P, _P, C.c_size_t, C.c_int64, _P]
+            L.lh_probe_stream.restype = C.c_int32
             for name, args in _PROTOS.items():
                 fn = getattr(L, name)
                 fn.argtypes = [_PD] + args

@@ -32,7 +32,57 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(float *out, i
   out[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;   // keeps the chains live
 }
 
+// Streaming HBM probe: 16 bytes per lane, UNROLL accesses in flight per
+// lane, grid-stride over the buffer.  MODE 0 copies src to dst, 1 only reads
+// src (a per-thread checksum goes to dst[thread]), 2 only writes dst.
+constexpr int kStreamUnroll = 4;
+
+template <int MODE>
+__global__ __launch_bounds__(kProbeThreads) void stream_probe_kernel(const uint4 *__restrict__ src,
+                                                                    uint4 *__restrict__ dst,
+                                                                    int64_t n16) {
+  const int64_t nthr = (int64_t)gridDim.x * kProbeThreads;
+  const int64_t t = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  uint32_t sum = 0;
+  for (int64_t i = t; i < n16; i += nthr * kStreamUnroll) {
+    uint4 v[kStreamUnroll];
+#pragma unroll
+    for (int k = 0; k < kStreamUnroll; ++k) {
+      const int64_t j = i + k * nthr;
+      if (MODE == 2) v[k] = make_uint4((uint32_t)j, 1u, 2u, 3u);
+      else if (j < n16) v[k] = src[j];
+    }
+#pragma unroll
+    for (int k = 0; k < kStreamUnroll; ++k) {
+      const int64_t j = i + k * nthr;
+      if (j < n16) {
+        if (MODE == 1) sum += v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+        else dst[j] = v[k];
+      }
+    }
+  }
+  if (MODE == 1) reinterpret_cast<uint32_t *>(dst)[t] = sum;
+}
+
 }  // namespace lh
+
+extern "C" lh_status lh_probe_stream(int32_t mode, const void *src, void *dst, size_t bytes,
+                                     int64_t blocks, lh_stream stream) {
+  if (mode < 0 || mode > 2 || bytes == 0 || bytes % 16 || !dst || (mode != 2 && !src) ||
+      !lh::grid_fits(blocks, lh::kProbeThreads) || blocks <= 0 ||
+      ((uintptr_t)src & 15) || ((uintptr_t)dst & 15))
+    return LH_ERR_INVALID_ARG;
+  (void)hipGetLastError();   // report this launch's error only
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const uint4 *s = (const uint4 *)src;
+  uint4 *d = (uint4 *)dst;
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((unsigned)blocks), blk(lh::kProbeThreads);
+  if (mode == 0) hipLaunchKernelGGL(lh::stream_probe_kernel<0>, grid, blk, 0, st, s, d, n16);
+  else if (mode == 1) hipLaunchKernelGGL(lh::stream_probe_kernel<1>, grid, blk, 0, st, s, d, n16);
+  else hipLaunchKernelGGL(lh::stream_probe_kernel<2>, grid, blk, 0, st, s, d, n16);
+  return lh::hip_status();
+}
 
 extern "C" lh_status lh_probe_mfma_bf16(int64_t blocks, int32_t iters, float *out,
                                         lh_stream stream) {

@@ -122,6 +122,7 @@ lh_status launch_transpose(const Geo &g, const void *rows, void *tr, hipStream_t
 // the previous stratum) into an LDS map, then the workgroup streams the
 // source rows out, CPR lanes per row, NF rows in flight per lane.
 constexpr int kScatChunk = 256;
+constexpr size_t kMaxLdsRows = 160 * 1024;   // LDS of one CU
 
 struct ScatArgs {
   const float *os;
@@ -258,66 +259,196 @@ struct ScatBwdArgs {
   bf16_t *dos_hi, *dos_lo;
   const float *os;
   float *drow;
-  int64_t N, S;
+  int64_t N, S, n_c, k_s;
   int32_t d;
 };
 
+// One workgroup per (stratum m, b*h).  The segments of stratum m's leaders
+// tile the tokens [T0, T1): T0 is the stratum's first anchor (its first row
+// is always a leader) and T1 the next stratum's first anchor (N after the
+// last stratum), since the last leader of a stratum holds up to there.  The
+// range is cut into one contiguous chunk per group of CPR lanes (a group
+// reads one token row per instruction, NF rows in flight per lane) and each
+// group sums its chunk in token order, segment by segment.  A segment that
+// starts and ends inside one chunk is finished by its group; a piece at a
+// chunk's start (segment begun in an earlier chunk) or end (continuing into
+// the next) goes to LDS, and the group where a segment starts adds the later
+// chunks' pieces in chunk order.  Every dO row is read once, the work is
+// balanced however long the segments are, and the sums run in a fixed order.
+// Tokens before the first anchor belong to no segment.  Rows that are not
+// leaders get zeros.
+constexpr int kScatBwdThreads = 256;
+
+template <int CPR>
+struct ScatBwdSmem {
+  static constexpr int G = kScatBwdThreads / CPR;   // groups of CPR lanes
+  float piece[2][G][CPR * 8];   // [0]: piece at a chunk's start, [1]: at its end
+  int32_t tag[2][G];            // leader index of each piece, -1: none
+  int32_t span[G];              // 1: the chunk lies inside one segment begun earlier
+  int32_t nl;                   // leaders of the stratum
+};
+
 template <typename T, int CPR>
-__global__ __launch_bounds__(256) void scatter_bwd_kernel(ScatBwdArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t bh = blockIdx.y;
-  if (j >= a.S) return;
-  const int d = a.d;
-  const int c = lane % CPR, u = lane / CPR;
-  constexpr int TL = 64 / CPR;
+__global__ __launch_bounds__(kScatBwdThreads) void scatter_bwd_kernel(ScatBwdArgs a) {
+  using Smem = ScatBwdSmem<CPR>;
+  constexpr int G = Smem::G;
+  extern __shared__ __align__(16) unsigned char sraw[];
+  Smem &sm = *reinterpret_cast<Smem *>(sraw);
+  const int nr = (int)(a.k_s + 1);
+  int32_t *la = reinterpret_cast<int32_t *>(sraw + sizeof(Smem));   // leader anchors
+  int32_t *lr = la + nr;                                             // leader rows
+  int32_t *cnt = lr + nr;                                            // [kScatBwdThreads]
+  const int tid = threadIdx.x;
+  const int64_t m = blockIdx.x, bh = blockIdx.y;
+  const int64_t row0 = m * nr;
   const int32_t *anc = a.anchor + bh * a.S;
-  const bool leader = (a.flags[bh * a.S + j] & LH_ROW_LEADER) != 0;
-  float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  if (leader) {
-    const int64_t t0 = max((int64_t)0, min((int64_t)anc[j], a.N));
-    int64_t nx = j + 1;
-    while (nx < a.S && anc[nx] == anc[j]) ++nx;
-    const int64_t t1 = max(t0, min(nx < a.S ? (int64_t)anc[nx] : a.N, a.N));
-    const T *dO = (const T *)a.dout + bh * a.N * d + c * 8;
-    // NF rows in flight per lane (raw, converted when added); each lane
-    // still adds its tokens in increasing order.  Segments average ~21
-    // tokens, so 8 per lane (32 per wavefront) covers most in one batch and
-    // keeps the registers low enough for 7 wavefronts per SIMD: the kernel
-    // is bound by each wavefront's chain of dependent loads, so resident
-    // wavefronts count for more than depth
-    constexpr int NF = 8;
-    for (int64_t t = t0 + u; t < t1; t += NF * TL) {
-      Raw8<T> x[NF];
-#pragma unroll
-      for (int k = 0; k < NF; ++k)
-        if (t + k * TL < t1) x[k].load(dO + (t + k * TL) * d);
-#pragma unroll
-      for (int k = 0; k < NF; ++k)
-        if (t + k * TL < t1) x[k].add_to(acc);
-    }
-#pragma unroll
-    for (int off = CPR; off < 64; off <<= 1)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], off);
+  const uint8_t *flg = a.flags + bh * a.S;
+  const int d = a.d;
+
+  // leaders of the stratum in row order: each thread counts its run of rows,
+  // an exclusive scan places them
+  const int q = (nr + kScatBwdThreads - 1) / kScatBwdThreads;
+  const int r_beg = min(nr, tid * q), r_end = min(nr, r_beg + q);
+  int c0 = 0;
+  for (int r = r_beg; r < r_end; ++r) c0 += (flg[row0 + r] & LH_ROW_LEADER) != 0;
+  cnt[tid] = c0;
+  __syncthreads();
+  for (int off = 1; off < kScatBwdThreads; off <<= 1) {
+    const int v = tid >= off ? cnt[tid - off] : 0;
+    __syncthreads();
+    cnt[tid] += v;
+    __syncthreads();
   }
-  const int64_t row = (bh * a.S + j) * d + c * 8;
-  if (u == 0) {
+  int pos = cnt[tid] - c0;
+  for (int r = r_beg; r < r_end; ++r)
+    if (flg[row0 + r] & LH_ROW_LEADER) {
+      la[pos] = anc[row0 + r];
+      lr[pos] = (int32_t)(row0 + r);
+      ++pos;
+    }
+  if (tid == kScatBwdThreads - 1) sm.nl = cnt[tid];
+  if (tid < G) {
+    sm.tag[0][tid] = sm.tag[1][tid] = -1;
+    sm.span[tid] = 0;
+  }
+  __syncthreads();
+  const int nl = sm.nl;
+  const int64_t T0 = nl > 0 ? max((int64_t)0, min((int64_t)la[0], a.N)) : a.N;
+  const int64_t T1 = m + 1 < a.n_c ? max(T0, min((int64_t)anc[row0 + nr], a.N)) : a.N;
+
+  const int g = tid / CPR, c = tid % CPR;
+  const T *dO = (const T *)a.dout + bh * a.N * d + c * 8;
+  // final value of leader k: dOS (and its split), drow = <dOS, OS>
+  auto finish = [&](int k, const float *acc) {
+    const int64_t row = (bh * a.S + lr[k]) * d + c * 8;
     if (a.dos) store8(a.dos + row, acc);
     if (a.dos_hi) store8_split(a.dos_hi + row, a.dos_lo + row, acc);
-  }
-  if (a.drow) {
-    float o[8];
-    load8(a.os + row, o);
-    float s = 0.f;
+    if (a.drow) {
+      float o[8];
+      load8(a.os + row, o);
+      float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s += acc[i] * o[i];
+      for (int i = 0; i < 8; ++i) s += acc[i] * o[i];
 #pragma unroll
-    for (int off = 1; off < CPR; off <<= 1) s += __shfl_xor(s, off);
-    if (lane == 0) a.drow[bh * a.S + j] = s;
+      for (int off = 1; off < CPR; off <<= 1) s += __shfl_xor(s, off);
+      if (c == 0) a.drow[bh * a.S + lr[k]] = s;
+    }
+  };
+
+  const int64_t n = nl > 0 ? T1 - T0 : 0;   // a valid selection has a leader per stratum
+  const int64_t C = (n + G - 1) / G;
+  const int64_t cb = T0 + g * C, ce = min(T1, cb + C);
+  if (cb < ce) {
+    // segment open at the chunk's start: the last leader with anchor <= cb
+    int lo = 0, hi = nl;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)la[mid] <= cb) lo = mid + 1; else hi = mid;
+    }
+    int k = lo - 1;                                   // >= 0: la[0] = T0 <= cb
+    int64_t nb = k + 1 < nl ? (int64_t)la[k + 1] : T1;   // end of segment k
+    bool begun_here = (int64_t)la[k] == cb;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    auto close = [&]() {   // segment k ends at nb <= ce
+      if (begun_here) {
+        finish(k, acc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm.piece[0][g][c * 8 + i] = acc[i];
+        if (c == 0) sm.tag[0][g] = k;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+      ++k;
+      nb = k + 1 < nl ? (int64_t)la[k + 1] : T1;
+      begun_here = true;
+    };
+    constexpr int NF = 8;
+    for (int64_t t0 = cb; t0 < ce; t0 += NF) {
+      Raw8<T> x[NF];
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        if (t0 + j < ce) x[j].load(dO + (t0 + j) * d);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) {
+        const int64_t t = t0 + j;
+        if (t < ce) {
+          while (t >= nb) close();
+          x[j].add_to(acc);
+        }
+      }
+    }
+    if (nb <= ce) {
+      close();   // the segment ends exactly at the chunk's end
+    } else if (begun_here) {
+      // begun in this chunk, continues: the piece at the chunk's end
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm.piece[1][g][c * 8 + i] = acc[i];
+      if (c == 0) sm.tag[1][g] = k;
+    } else {
+      // the whole chunk lies inside a segment begun earlier that goes on
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm.piece[0][g][c * 8 + i] = acc[i];
+      if (c == 0) {
+        sm.tag[0][g] = k;
+        sm.span[g] = 1;
+      }
+    }
   }
+  __syncthreads();
+  // segments that cross chunks: the group where one begins adds the pieces
+  // of the following chunks in order, up to the chunk where it ends
+  if (sm.tag[1][g] >= 0) {
+    const int k = sm.tag[1][g];
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = sm.piece[1][g][c * 8 + i];
+    for (int h = g + 1; h < G && sm.tag[0][h] == k; ++h) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += sm.piece[0][h][c * 8 + i];
+      if (!sm.span[h]) break;
+    }
+    finish(k, acc);
+  }
+  // rows that are not leaders: zeros
+  const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = g; r < nr; r += G) {
+    if (flg[row0 + r] & LH_ROW_LEADER) continue;
+    const int64_t row = (bh * a.S + row0 + r) * d + c * 8;
+    if (a.dos) store8(a.dos + row, zero);
+    if (a.dos_hi) {
+      store8(a.dos_hi + row, zero);
+      store8(a.dos_lo + row, zero);
+    }
+    if (a.drow && c == 0) a.drow[bh * a.S + row0 + r] = 0.f;
+  }
+}
+
+static size_t scatter_bwd_lds(const Geo &g) {
+  const size_t fixed = g.d == 128 ? sizeof(ScatBwdSmem<16>) : sizeof(ScatBwdSmem<8>);
+  return fixed + (2 * (size_t)(g.k_s + 1) + kScatBwdThreads) * sizeof(int32_t);
 }
 
 lh_status launch_scatter_bwd(const Geo &g, const void *dout, const int32_t *sel_anchor,
@@ -326,16 +457,24 @@ lh_status launch_scatter_bwd(const Geo &g, const void *dout, const int32_t *sel_
   ScatBwdArgs a;
   a.dout = dout; a.anchor = sel_anchor; a.flags = sel_flags; a.dos = dos;
   a.dos_hi = dos_lo ? dos_hi : nullptr; a.dos_lo = dos_lo;
-  a.os = os; a.drow = os ? drow : nullptr; a.N = g.N; a.S = g.S; a.d = g.d;
-  dim3 grid(cdiv(g.S, 4), (unsigned)g.BH());
+  a.os = os; a.drow = os ? drow : nullptr; a.N = g.N; a.S = g.S; a.n_c = g.n_c; a.k_s = g.k_s;
+  a.d = g.d;
+  const size_t shm = scatter_bwd_lds(g);
+  if (shm > kMaxLdsRows) return LH_ERR_UNSUPPORTED;
+  dim3 grid((unsigned)g.n_c, (unsigned)g.BH());
+#define LH_SBWD(T, C)                                                                         \
+  do {                                                                                        \
+    (void)hipFuncSetAttribute((const void *)scatter_bwd_kernel<T, C>,                         \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);          \
+    hipLaunchKernelGGL((scatter_bwd_kernel<T, C>), grid, dim3(kScatBwdThreads), shm, st, a);  \
+  } while (0)
   // dO and OS both have the output type
   if (g.out == LH_BF16) {
-    if (g.d == 128) hipLaunchKernelGGL((scatter_bwd_kernel<bf16_t, 16>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((scatter_bwd_kernel<bf16_t, 8>), grid, dim3(256), 0, st, a);
+    if (g.d == 128) LH_SBWD(bf16_t, 16); else LH_SBWD(bf16_t, 8);
   } else {
-    if (g.d == 128) hipLaunchKernelGGL((scatter_bwd_kernel<float, 16>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((scatter_bwd_kernel<float, 8>), grid, dim3(256), 0, st, a);
+    if (g.d == 128) LH_SBWD(float, 16); else LH_SBWD(float, 8);
   }
+#undef LH_SBWD
   return hip_status();
 }
 
@@ -742,7 +881,9 @@ lh_status check_rows_supported(const Geo &g) {
   const bool ok = grid_fits(cdiv(S, 256 / cpr), 256) &&            // gather
                   grid_fits(g.Sp / 64, 256) &&                      // transpose
                   grid_fits(g.n_c * (int64_t)cdiv(g.Bc, kScatChunk), 256) &&   // scatter
-                  grid_fits(cdiv(S, 4), 256) &&                     // scatter adjoints
+                  grid_fits(g.n_c, kScatBwdThreads) &&              // scatter adjoint
+                  scatter_bwd_lds(g) <= kMaxLdsRows &&
+                  grid_fits(cdiv(S, 4), 256) &&                     // span adjoint
                   grid_fits(cdiv(N * row_vec, 256), 256) &&         // copy_rows
                   grid_fits(cdiv(N, 256), 256) &&                   // owner
                   grid_fits(cdiv(N, (256 / cpr) * 8), 256) &&       // span scatter

@@ -246,3 +246,13 @@ def test_validate_rejects_grids_past_32_bits(lib):
     assert lib.lh_validate(C.byref(dd)) == L.LH_ERR_UNSUPPORTED
     dd.H = 128
     assert lib.lh_validate(C.byref(dd)) == L.LH_OK
+
+
+def test_stream_probe_rejects_bad_args_without_launch(lib):
+    p = C.c_void_p(0x1000)   # never dereferenced: every case fails validation first
+    for mode, src, dst, nbytes, blocks in ((3, p, p, 4096, 8), (0, None, p, 4096, 8),
+                                           (0, p, None, 4096, 8), (1, p, p, 4100, 8),
+                                           (2, None, p, 0, 8), (0, p, p, 4096, 0),
+                                           (0, p, p, 4096, 1 << 24), (0, C.c_void_p(0x1008), p, 4096, 8)):
+        st = lib.lh_probe_stream(mode, src, dst, nbytes, blocks, None)
+        assert st == L.LH_ERR_INVALID_ARG, (mode, nbytes, blocks, st)
