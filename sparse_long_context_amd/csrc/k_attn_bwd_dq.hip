@@ -33,8 +33,10 @@ static_assert(kQBK == kKeyBlock, "dQ streams the shared key blocks");
 template <int D>
 using QStage = KeyStage<D>;
 
+// d = 128 needs more than 256 registers (one wavefront per SIMD); d = 64
+// fits 256, so two workgroups share each CU
 template <int D>
-__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
 void attn_bwd_dq_kernel(
     const bf16_t *__restrict__ qs, const bf16_t *__restrict__ ks, const bf16_t *__restrict__ vs,
     const bf16_t *__restrict__ doh, const bf16_t *__restrict__ dol,
