@@ -91,8 +91,9 @@ KERNEL_OF = {
 
 
 def counters_for(kernel: str, workload_name: str):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source (else None)."""
+    """The committed rocprofv3 counter record of a kernel (HBM bytes per
+    launch; for the MFMA kernels also MFMA busy share and issued/algorithmic
+    work), if it was taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
@@ -110,7 +111,7 @@ def counters_for(kernel: str, workload_name: str):
         h.update(open(src, "rb").read())
     if h.hexdigest() != rec["sha256"]:
         return None
-    return rec.get("bytes_per_launch")
+    return rec
 
 
 def cpu_baseline(w, Q, K, V, dO):
@@ -453,12 +454,22 @@ def main():
         name = max((n for n in stages if n in KERNEL_OF), key=lambda n: stages[n]["ms"])
         t = stages[name]["ms"] / 1e3
         ach = work[name] / t / 1e12
-        traffic = counters_for(KERNEL_OF[name], w.name)
+        rec = counters_for(KERNEL_OF[name], w.name)
+        traffic = rec.get("bytes_per_launch") if rec else None
         roof = {"kernel": KERNEL_OF[name], "bound": "mfma", "achieved": round(ach, 2),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "avg_launch_ms": round(stages[name]["ms"], 4),
                 "frac_of_measured_peak": round(ach / peaks["mfma_bf16_TFLOPs"], 4),
                 "algorithmic_per_launch": work[name]}
+        roof["mfma_busy"] = rec.get("mfma_busy") if rec else None
+        roof["mfma_work_ratio"] = rec.get("mfma_work_ratio") if rec else None
+        # MFMA busy share and issued/algorithmic MFMA work of each attention
+        # kernel, from the committed counter record of the current source
+        for n, kern in KERNEL_OF.items():
+            r_ = counters_for(kern, w.name)
+            if n in stages and r_:
+                stages[n]["mfma_busy"] = r_.get("mfma_busy")
+                stages[n]["mfma_work_ratio"] = r_.get("mfma_work_ratio")
         for n, e in stages.items():
             print(f"[bench] stage {n:20s} {e}", file=sys.stderr, flush=True)
 
