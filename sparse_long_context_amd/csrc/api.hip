@@ -744,12 +744,21 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
     const float *in_kv[2] = {dks, dvs};
     void *out_kv[2] = {grad[1], grad[2]};
     LH_TRY(launch_unpool(g, in_kv, s->row_of, out_kv, 2, side));
-    LH_TRY(launch_attn_bwd_dq_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
-                                   (const bf16_t *)s->vs, dhi, dlo, s->lse, drow, s->sel_flags,
-                                   dqs, st));
-    const float *in_q[1] = {dqs};
-    void *out_q[1] = {grad[0]};
-    LH_TRY(launch_unpool(g, in_q, s->row_of, out_q, 1, st));
+    if (dq_can_unpool(g)) {
+      // every dQ workgroup's 128 rows are whole strata: it runs the gather +
+      // pooling adjoint of its own rows in its epilogue (no dQS round trip,
+      // and dQ's token writes overlap other workgroups' MFMA work)
+      LH_TRY(launch_attn_bwd_dq_unpool(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
+                                       (const bf16_t *)s->vs, dhi, dlo, s->lse, drow,
+                                       s->sel_flags, s->row_of, grad[0], st));
+    } else {
+      LH_TRY(launch_attn_bwd_dq_bf16(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
+                                     (const bf16_t *)s->vs, dhi, dlo, s->lse, drow, s->sel_flags,
+                                     dqs, st));
+      const float *in_q[1] = {dqs};
+      void *out_q[1] = {grad[0]};
+      LH_TRY(launch_unpool(g, in_q, s->row_of, out_q, 1, st));
+    }
     LH_TRY(sj.join());
   } else {
     float *dos = (float *)c.take(z.subseq_f32);

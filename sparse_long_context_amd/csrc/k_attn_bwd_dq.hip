@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "lh_mfma.h"
+#include "lh_unpool.h"
 
 namespace lh {
 
@@ -35,14 +36,18 @@ using QStage = KeyStage<D>;
 
 // d = 128 needs more than 256 registers (one wavefront per SIMD); d = 64
 // fits 256, so two workgroups share each CU
-template <int D>
+// EPI: 0 = dQS rows only; 1 (bf16) or 2 (float32) = instead, the layer's dQ
+// of the workgroup's strata (its 128 rows are whole strata): the rows go to
+// LDS and the gather + pooling adjoint runs from there (lh_unpool.h), so the
+// token writes overlap other workgroups' MFMA work.
+template <int D, int EPI>
 __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
 void attn_bwd_dq_kernel(
     const bf16_t *__restrict__ qs, const bf16_t *__restrict__ ks, const bf16_t *__restrict__ vs,
     const bf16_t *__restrict__ doh, const bf16_t *__restrict__ dol,
     const float *__restrict__ lse, const float *__restrict__ drow,
     const uint8_t *__restrict__ flags, float *__restrict__ dqs, int64_t S, int32_t BH,
-    float scale) {
+    float scale, UnpoolArgs ua, int32_t rps) {
   static_assert(kQStages == 5, "block kb + 4 is issued into the slot of block kb - 1");
   extern __shared__ __align__(16) unsigned char smraw[];
   QStage<D> *stg = reinterpret_cast<QStage<D> *>(smraw);
@@ -309,28 +314,71 @@ void attn_bwd_dq_kernel(
     }
   }
 
-  if (q < S) {
-    float *out = dqs + (bh * S + q) * D;
-    // lane: query column; rows are head-dim 8I + 4h + J
+  if constexpr (EPI == 0) {
+    if (q < S) {
+      float *out = dqs + (bh * S + q) * D;
+      // lane: query column; rows are head-dim 8I + 4h + J
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+      for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        float o4[4];
+        for (int I = 0; I < 4; ++I) {
+          float o4[4];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) o4[J] = acc_dq[b][4 * I + J] * scale;
-        *reinterpret_cast<float4 *>(out + b * 32 + 8 * I + 4 * h) =
-            make_float4(o4[0], o4[1], o4[2], o4[3]);
-      }
+          for (int J = 0; J < 4; ++J) o4[J] = acc_dq[b][4 * I + J] * scale;
+          *reinterpret_cast<float4 *>(out + b * 32 + 8 * I + 4 * h) =
+              make_float4(o4[0], o4[1], o4[2], o4[3]);
+        }
+    }
+  } else {
+    // every wavefront is past its last ring read (and every copy into the
+    // ring has landed: the last iterations wait for vmcnt(0))
+    __syncthreads();
+    using TO = typename std::conditional<EPI == 1, bf16_t, float>::type;
+    const int64_t row0 = (int64_t)qb * kQBQ;
+    const int nrows = (int)min((int64_t)kQBQ, S - row0);
+    float *rows = reinterpret_cast<float *>(smraw);                          // [kQBQ][D]
+    int32_t *ro = reinterpret_cast<int32_t *>(smraw + (size_t)kQBQ * D * 4);  // staged row_of
+    if (q < S) {
+      float *dst = rows + (q - row0) * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          float o4[4];
+#pragma unroll
+          for (int J = 0; J < 4; ++J) o4[J] = acc_dq[b][4 * I + J] * scale;
+          *reinterpret_cast<f32x4 *>(dst + b * 32 + 8 * I + 4 * h) = {o4[0], o4[1], o4[2], o4[3]};
+        }
+    }
+    const int64_t m0 = row0 / rps;
+    const int spw = nrows / rps;
+    unpool_stage_ro<kQThreads>(ua, ro, ua.row_of + bh * ua.E, m0, spw, row0, row0 + nrows, tid);
+    __syncthreads();
+    const float *lr = rows + (tid % (D / 8)) * 8;
+    auto ld = [&](int32_t r, float *x) {   // r in [row0, row0 + nrows): staged so
+      const float *p = lr + (int)(r - row0) * D;
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+      x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+      x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+    };
+    unpool_strata<TO, D / 8, kQThreads>(ua, ro, ld, (TO *)ua.dx[0] + (bh * ua.N + m0 * ua.Bc) * D,
+                                        spw, tid);
   }
 }
 
 
 // LDS of one dQ workgroup: the ring, then one REDUNDANT bit per key of the
-// widest key range
-static size_t dq_lds(const Geo &g) {
+// widest key range; with the pooling adjoint in the epilogue, at least the
+// workgroup's rows and its strata's staged row_of
+static size_t dq_lds(const Geo &g, bool unpool) {
   const size_t ring = g.d == 128 ? sizeof(QStage<128>) * kQStages : sizeof(QStage<64>) * kQStages;
-  return ring + (size_t)((g.S + 63) / 64 * 8);
+  size_t b = ring + (size_t)((g.S + 63) / 64 * 8);
+  if (unpool) {
+    const size_t e = (size_t)kQBQ * g.d * 4 + (size_t)(kQBQ / (g.k_s + 1)) * g.T * 4;
+    b = b > e ? b : e;
+  }
+  return b;
 }
 
 // bf16 I/O: one head's rows fit a buffer resource, the grid's work-items
@@ -339,27 +387,63 @@ lh_status check_attn_dq_supported(const Geo &g) {
   if (g.io != LH_BF16) return LH_OK;
   if (!rsrc_fits(g)) return LH_ERR_UNSUPPORTED;
   if (!grid_fits((int64_t)cdiv(g.S, kQBQ) * g.BH(), kQThreads)) return LH_ERR_UNSUPPORTED;
-  return dq_lds(g) <= kMaxLds ? LH_OK : LH_ERR_UNSUPPORTED;
+  return dq_lds(g, false) <= kMaxLds ? LH_OK : LH_ERR_UNSUPPORTED;
+}
+
+// whether the dQ kernel can run the pooling adjoint of its own rows: every
+// workgroup's 128 rows are whole strata, and the epilogue's LDS stays within
+// the budget that keeps the kernel's occupancy (two workgroups per CU at
+// d = 64)
+bool dq_can_unpool(const Geo &g) {
+  if (g.io != LH_BF16 || kQBQ % (g.k_s + 1) != 0 || g.T > kUnpoolLdsEntries) return false;
+  const size_t cap = g.d == 64 ? kMaxLds / 2 : kMaxLds;
+  return dq_lds(g, true) <= cap && dq_lds(g, false) <= cap;
+}
+
+static lh_status launch_dq(const Geo &g, const bf16_t *qs, const bf16_t *ks, const bf16_t *vs,
+                           const bf16_t *dos_hi, const bf16_t *dos_lo, const float *lse,
+                           const float *drow, const uint8_t *flags, float *dqs,
+                           const int32_t *row_of, void *dq, hipStream_t st) {
+  if (check_attn_dq_supported(g) != LH_OK) return LH_ERR_UNSUPPORTED;
+  const bool unpool = dq != nullptr;
+  if (unpool && !dq_can_unpool(g)) return LH_ERR_UNSUPPORTED;
+  const unsigned items = cdiv(g.S, kQBQ) * (unsigned)g.BH();
+  const size_t shm = dq_lds(g, unpool);
+  UnpoolArgs ua = make_unpool_args(g, unpool ? kQBQ / (int)(g.k_s + 1) : 1);
+  ua.row_of = row_of;
+  ua.dx[0] = dq;
+  const int32_t rps = (int32_t)(g.k_s + 1);
+  const int epi = unpool ? (g.out == LH_BF16 ? 1 : 2) : 0;
+#define LH_DQ(D, E)                                                                           \
+  do {                                                                                        \
+    (void)hipFuncSetAttribute((const void *)attn_bwd_dq_kernel<D, E>,                         \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);          \
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, E>), dim3(items), dim3(kQThreads), shm, st, qs, \
+                       ks, vs, dos_hi, dos_lo, lse, drow, flags, dqs, g.S, (int32_t)g.BH(),   \
+                       g.scale, ua, rps);                                                     \
+  } while (0)
+  if (g.d == 128) {
+    if (epi == 0) LH_DQ(128, 0); else if (epi == 1) LH_DQ(128, 1); else LH_DQ(128, 2);
+  } else {
+    if (epi == 0) LH_DQ(64, 0); else if (epi == 1) LH_DQ(64, 1); else LH_DQ(64, 2);
+  }
+#undef LH_DQ
+  return hip_status();
 }
 
 lh_status launch_attn_bwd_dq_bf16(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                   const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
                                   const float *lse, const float *drow, const uint8_t *flags,
                                   float *dqs, hipStream_t st) {
-  if (check_attn_dq_supported(g) != LH_OK) return LH_ERR_UNSUPPORTED;
-  const unsigned items = cdiv(g.S, kQBQ) * (unsigned)g.BH();
-  const size_t shm = dq_lds(g);
-#define LH_DQ(D)                                                                              \
-  do {                                                                                        \
-    (void)hipFuncSetAttribute((const void *)attn_bwd_dq_kernel<D>,                            \
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);          \
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(items), dim3(kQThreads), shm, st, qs, ks,  \
-                       vs, dos_hi, dos_lo, lse, drow, flags, dqs, g.S, (int32_t)g.BH(),       \
-                       g.scale);                                                              \
-  } while (0)
-  if (g.d == 128) LH_DQ(128); else LH_DQ(64);
-#undef LH_DQ
-  return hip_status();
+  return launch_dq(g, qs, ks, vs, dos_hi, dos_lo, lse, drow, flags, dqs, nullptr, nullptr, st);
+}
+
+lh_status launch_attn_bwd_dq_unpool(const Geo &g, const bf16_t *qs, const bf16_t *ks,
+                                    const bf16_t *vs, const bf16_t *dos_hi,
+                                    const bf16_t *dos_lo, const float *lse, const float *drow,
+                                    const uint8_t *flags, const int32_t *row_of, void *dq,
+                                    hipStream_t st) {
+  return launch_dq(g, qs, ks, vs, dos_hi, dos_lo, lse, drow, flags, nullptr, row_of, dq, st);
 }
 
 }  // namespace lh

@@ -13,7 +13,7 @@
 // Scatter reading (design notes, causal hold): token t takes the output of
 // the LEADER row with the largest anchor <= t; tokens before the first anchor
 // take 0.  A leader's hold segment is [its anchor, next leader's anchor).
-#include "lh_internal.h"
+#include "lh_unpool.h"
 
 namespace lh {
 
@@ -724,54 +724,8 @@ lh_status launch_dos_prep(const Geo &g, const float *dos, const float *os, bf16_
 }
 
 // ---------------------------------------------------------------- unpool
-// dx[t] = sum_l dxs[row_of(l, t / p^l)] / p^l over the selected ancestors of
-// t.  One workgroup covers `spw` whole strata of one (b, h) and one tensor.
-// Their row_of entries are staged in LDS level by level (level l of strata
-// m0 .. m0+spw-1 is one contiguous run of row_of), so the level-l ancestor of
-// workgroup-local token u sits at lb[l] + u / p^l.  A thread owns a
-// contiguous run of level-1 entries (CPR lanes per row).  Levels L-1 .. 2 are
-// summed once per level-2 cell (coarsest first) and kept; each entry adds its
-// level-1 row, converts that sum once, and every token without a level-0 row
-// of its own stores it unchanged; the others add their row.  The summation
-// order is fixed, so results are reproducible.
-constexpr int kUnpoolThreads = 256;
-constexpr int kUnpoolLdsEntries = 8192;   // row_of entries staged per workgroup
-
-struct UnpoolArgs {
-  const float *dxs[3];
-  void *dx[3];
-  const int32_t *row_of;
-  int64_t N, E, S, Bc;
-  int32_t d, L, p, spw, lgp;    // lgp = log2(p) when p is a power of two, else -1
-  int64_t loff[kMaxLevels];
-  int32_t per[kMaxLevels];      // entries of level l per stratum (Bc / p^l)
-  int32_t pw[kMaxLevels];       // p^l
-  int32_t lb[kMaxLevels];       // first LDS slot of level l (spw * entries below it)
-  float inv[kMaxLevels];
-};
-
-// 8 output values in the output dtype, as stored by one 16- or 32-byte write
-template <typename TO> struct Pack8;
-template <> struct Pack8<bf16_t> {
-  uint4 w;
-  __device__ void set(const float *x) {
-    w = make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]), pack2_bf16(x[4], x[5]),
-                   pack2_bf16(x[6], x[7]));
-  }
-  __device__ void put(bf16_t *p) const { *reinterpret_cast<uint4 *>(p) = w; }
-};
-template <> struct Pack8<float> {
-  float4 a, b;
-  __device__ void set(const float *x) {
-    a = make_float4(x[0], x[1], x[2], x[3]);
-    b = make_float4(x[4], x[5], x[6], x[7]);
-  }
-  __device__ void put(float *p) const {
-    *reinterpret_cast<float4 *>(p) = a;
-    *reinterpret_cast<float4 *>(p + 4) = b;
-  }
-};
-
+// One workgroup per group of `spw` whole strata of one (b, h) and one tensor
+// (the summation itself is unpool_strata in lh_unpool.h).
 template <typename TO, int CPR>
 __global__ __launch_bounds__(kUnpoolThreads) void unpool_kernel(UnpoolArgs a) {
   extern __shared__ int32_t ro[];
@@ -779,89 +733,12 @@ __global__ __launch_bounds__(kUnpoolThreads) void unpool_kernel(UnpoolArgs a) {
   const int64_t bh = blockIdx.y;
   const int64_t m0 = (int64_t)blockIdx.x * a.spw;   // first stratum of the workgroup
   const int tid = threadIdx.x;
-  const int32_t *rog = a.row_of + bh * a.E;
-  for (int l = 0; l < a.L; ++l) {
-    const int cnt = a.spw * a.per[l];
-    const int32_t *src = rog + a.loff[l] + m0 * a.per[l];
-    for (int i = tid; i < cnt; i += kUnpoolThreads) {
-      const int32_t r = src[i];
-      ro[a.lb[l] + i] = (r >= 0 && r < a.S) ? r : -1;
-    }
-  }
+  unpool_stage_ro<kUnpoolThreads>(a, ro, a.row_of + bh * a.E, m0, a.spw, 0, a.S, tid);
   __syncthreads();
-  const int c = tid % CPR;
-  constexpr int LANES = kUnpoolThreads / CPR;   // lanes along the tokens
-  const int d = a.d;
-  const float *dxs = a.dxs[z] + bh * a.S * d + c * 8;
-  TO *out = (TO *)a.dx[z] + (bh * a.N + m0 * a.Bc) * d + c * 8;
-  const int ntok = a.spw * (int)a.Bc;
-  const int P1 = a.L >= 2 ? a.p : 1;    // tokens per level-1 entry
-  const int nent = ntok / P1;
-  const int span = (nent + LANES - 1) / LANES;
-  const int e_begin = (tid / CPR) * span, e_end = min(nent, e_begin + span);
-  auto anc = [&](int u, int l) { return a.lgp >= 0 ? (u >> (a.lgp * l)) : u / a.pw[l]; };
-  float A2[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) A2[i] = 0.f;
-  int cell = -1;
-  for (int e = e_begin; e < e_end; ++e) {
-    const int u0 = e * P1;
-    if (a.L >= 3 && anc(u0, 2) != cell) {   // levels L-1 .. 2, coarsest first
-      cell = anc(u0, 2);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) A2[i] = 0.f;
-      for (int l = a.L - 1; l >= 2; --l) {
-        const int32_t r = ro[a.lb[l] + anc(u0, l)];
-        if (r >= 0) {
-          float x[8];
-          load8(dxs + (int64_t)r * d, x);
-          const float w = a.inv[l];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) A2[i] += x[i] * w;
-        }
-      }
-    }
-    float A[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) A[i] = A2[i];
-    if (a.L >= 2) {
-      const int32_t r = ro[a.lb[1] + e];
-      if (r >= 0) {
-        float x[8];
-        load8(dxs + (int64_t)r * d, x);
-        const float w = a.inv[1];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) A[i] += x[i] * w;
-      }
-    }
-    Pack8<TO> shared_row;
-    shared_row.set(A);
-    TO *orow = out + (int64_t)u0 * d;
-    for (int k0 = 0; k0 < P1; k0 += 4) {
-      float x[4][8];
-      int32_t r[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        r[k] = k0 + k < P1 ? ro[u0 + k0 + k] : -1;   // level 0 starts at slot 0
-        if (r[k] >= 0) load8(dxs + (int64_t)r[k] * d, x[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (k0 + k >= P1) break;
-        TO *dst = orow + (k0 + k) * d;
-        if (r[k] >= 0) {
-          float o[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = A[i] + x[k][i];
-          Pack8<TO> v;
-          v.set(o);
-          v.put(dst);
-        } else {
-          shared_row.put(dst);
-        }
-      }
-    }
-  }
+  const float *dxs = a.dxs[z] + bh * a.S * a.d + (tid % CPR) * 8;
+  auto rows = [&](int32_t r, float *x) { load8(dxs + (int64_t)r * a.d, x); };
+  unpool_strata<TO, CPR, kUnpoolThreads>(a, ro, rows, (TO *)a.dx[z] + (bh * a.N + m0 * a.Bc) * a.d,
+                                         a.spw, tid);
 }
 
 static int unpool_spw(const Geo &g) {
@@ -893,18 +770,15 @@ lh_status check_rows_supported(const Geo &g) {
   return g.T <= kUnpoolLdsEntries ? LH_OK : LH_ERR_UNSUPPORTED;
 }
 
-lh_status launch_unpool(const Geo &g, const float *const dxs[], const int32_t *row_of,
-                        void *const dx[], int nt, hipStream_t st) {
-  if (g.T > kUnpoolLdsEntries) return LH_ERR_UNSUPPORTED;
-  if (nt < 1 || nt > 3) return LH_ERR_INVALID_ARG;
+UnpoolArgs make_unpool_args(const Geo &g, int spw) {
   UnpoolArgs a;
   for (int i = 0; i < 3; ++i) {
-    a.dxs[i] = i < nt ? dxs[i] : nullptr;
-    a.dx[i] = i < nt ? dx[i] : nullptr;
+    a.dxs[i] = nullptr;
+    a.dx[i] = nullptr;
   }
-  a.row_of = row_of; a.N = g.N; a.E = g.E; a.S = g.S; a.Bc = g.Bc; a.d = g.d; a.L = g.L;
-  a.p = g.p;
-  a.spw = unpool_spw(g);
+  a.row_of = nullptr;
+  a.N = g.N; a.E = g.E; a.S = g.S; a.Bc = g.Bc; a.d = g.d; a.L = g.L; a.p = g.p;
+  a.spw = spw;
   a.lgp = -1;
   for (int k = 0; k < 31; ++k)
     if ((1 << k) == g.p) a.lgp = k;
@@ -915,8 +789,21 @@ lh_status launch_unpool(const Geo &g, const float *const dxs[], const int32_t *r
     a.per[l] = l < g.L ? (int32_t)(g.Bc / g.pw[l]) : 0;
     a.inv[l] = l < g.L ? (float)(1.0 / (double)g.pw[l]) : 0.f;
     a.lb[l] = lb;
-    lb += a.spw * a.per[l];
+    lb += spw * a.per[l];
   }
+  return a;
+}
+
+lh_status launch_unpool(const Geo &g, const float *const dxs[], const int32_t *row_of,
+                        void *const dx[], int nt, hipStream_t st) {
+  if (g.T > kUnpoolLdsEntries) return LH_ERR_UNSUPPORTED;
+  if (nt < 1 || nt > 3) return LH_ERR_INVALID_ARG;
+  UnpoolArgs a = make_unpool_args(g, unpool_spw(g));
+  for (int i = 0; i < nt; ++i) {
+    a.dxs[i] = dxs[i];
+    a.dx[i] = dx[i];
+  }
+  a.row_of = row_of;
   const size_t smem = (size_t)a.spw * g.T * sizeof(int32_t);
   dim3 grid((unsigned)(g.n_c / a.spw), (unsigned)g.BH(), (unsigned)nt);
   if (g.out == LH_BF16) {

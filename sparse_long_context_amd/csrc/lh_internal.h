@@ -185,6 +185,16 @@ lh_status launch_attn_bwd_dq_bf16(const Geo &g, const bf16_t *qs, const bf16_t *
                                   const bf16_t *vs, const bf16_t *dos_hi, const bf16_t *dos_lo,
                                   const float *lse, const float *drow, const uint8_t *flags,
                                   float *dqs, hipStream_t st);
+// The same dQ kernel with the gather + pooling adjoint of its own rows in
+// the epilogue (the layer backward): dq [BH, N, d] of the output type
+// instead of the float32 subsequence rows.  Only where every workgroup's
+// 128 rows are whole strata and the epilogue's LDS fits (dq_can_unpool).
+bool dq_can_unpool(const Geo &g);
+lh_status launch_attn_bwd_dq_unpool(const Geo &g, const bf16_t *qs, const bf16_t *ks,
+                                    const bf16_t *vs, const bf16_t *dos_hi,
+                                    const bf16_t *dos_lo, const float *lse, const float *drow,
+                                    const uint8_t *flags, const int32_t *row_of, void *dq,
+                                    hipStream_t st);
 // float32 dos [BH,S,d] -> optional bf16 split (hi, lo) and drow = rowsum(dos * os)
 lh_status launch_dos_prep(const Geo &g, const float *dos, const float *os, bf16_t *dos_hi,
                           bf16_t *dos_lo, float *drow, hipStream_t st);
