@@ -130,7 +130,7 @@ __device__ __forceinline__ void scatter_hold(unsigned char *smraw, int32_t *ep,
       } while (t >= nb);
       val = piece();
     }
-    *reinterpret_cast<uint4 *>(dst + t * RB) = val;
+    store16_nt(dst + t * RB, val);   // the layer output: streamed out
   }
 }
 

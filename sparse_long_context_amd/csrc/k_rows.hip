@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < NF; ++k)
-      if (tb + k * TW < ntok) store8(o + (int64_t)(tb + k * TW) * d, x[k]);
+      if (tb + k * TW < ntok) store8_nt(o + (int64_t)(tb + k * TW) * d, x[k]);
   }
 }
 
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(256) void scatter_span_kernel(const float *os, cons
   }
 #pragma unroll
   for (int k = 0; k < NF; ++k)
-    if (t0 + k * TW < N) store8(o + (t0 + k * TW) * d, x[k]);
+    if (t0 + k * TW < N) store8_nt(o + (t0 + k * TW) * d, x[k]);
 }
 
 lh_status launch_scatter_span(const Geo &g, const float *os, const int32_t *owner, void *o,

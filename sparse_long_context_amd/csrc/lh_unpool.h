@@ -48,7 +48,7 @@ template <> struct Pack8<bf16_t> {
     w = make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]), pack2_bf16(x[4], x[5]),
                    pack2_bf16(x[6], x[7]));
   }
-  __device__ void put(bf16_t *p) const { *reinterpret_cast<uint4 *>(p) = w; }
+  __device__ void put(bf16_t *p) const { store16_nt(p, w); }   // gradients: streamed out
 };
 template <> struct Pack8<float> {
   float4 a, b;
@@ -57,8 +57,10 @@ template <> struct Pack8<float> {
     b = make_float4(x[4], x[5], x[6], x[7]);
   }
   __device__ void put(float *p) const {
-    *reinterpret_cast<float4 *>(p) = a;
-    *reinterpret_cast<float4 *>(p + 4) = b;
+    store16_nt(p, make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
+                             __float_as_uint(a.w)));
+    store16_nt(p + 4, make_uint4(__float_as_uint(b.x), __float_as_uint(b.y),
+                                 __float_as_uint(b.z), __float_as_uint(b.w)));
   }
 };
 
