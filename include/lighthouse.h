@@ -37,7 +37,11 @@
  *    keeps (default priority), forked from `stream` and joined back to it by
  *    events, so that they are complete whenever `stream`'s work is.  No call
  *    synchronises or reads device memory back to the host.
- *  - Outputs are overwritten, never accumulated.
+ *  - Outputs are overwritten, never accumulated.  Token-length outputs that
+ *    no later kernel of the layer reads (the layer output, the input
+ *    gradients, the scatter stages' outputs) are written with nontemporal
+ *    stores: they go to HBM rather than staying dirty in the caches, so a
+ *    consumer reads them from HBM.
  *  - Errors: every call validates its dims and pointers first and returns a
  *    negative lh_status without launching anything if they are invalid.
  *    lh_validate applies every limit a launch has (grid sizes, LDS budgets,
