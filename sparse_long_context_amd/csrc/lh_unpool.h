@@ -1,6 +1,6 @@
 // The gather and pooling adjoint (unpool) of whole strata, shared by the
-// unpool kernel and the epilogues of the attention backward kernels that
-// hold whole strata's subsequence rows (gist.science explainer "Long Context
+// unpool kernel and the epilogue of the dQ kernel, whose workgroups hold
+// whole strata's subsequence rows (gist.science explainer "Long Context
 // Pre-Training with Lighthouse Attention", technical summary 2.B: gradients
 // reach the pooled inputs through gather and pooling only):
 //   dx[t] = sum over levels l of dxs[row_of(l, t / p^l)] / p^l,
