@@ -297,7 +297,8 @@ __global__ __launch_bounds__(kScatBwdThreads) void scatter_bwd_kernel(ScatBwdArg
   const int nr = (int)(a.k_s + 1);
   int32_t *la = reinterpret_cast<int32_t *>(sraw + sizeof(Smem));   // leader anchors
   int32_t *lr = la + nr;                                             // leader rows
-  int32_t *cnt = lr + nr;                                            // [kScatBwdThreads]
+  int32_t *wtot = lr + nr;                          // [kScatBwdThreads / 64] wave counts
+  uint8_t *lead = reinterpret_cast<uint8_t *>(wtot + kScatBwdThreads / 64);   // [nr]
   const int tid = threadIdx.x;
   const int64_t m = blockIdx.x, bh = blockIdx.y;
   const int64_t row0 = m * nr;
@@ -305,28 +306,39 @@ __global__ __launch_bounds__(kScatBwdThreads) void scatter_bwd_kernel(ScatBwdArg
   const uint8_t *flg = a.flags + bh * a.S;
   const int d = a.d;
 
-  // leaders of the stratum in row order: each thread counts its run of rows,
-  // an exclusive scan places them
-  const int q = (nr + kScatBwdThreads - 1) / kScatBwdThreads;
-  const int r_beg = min(nr, tid * q), r_end = min(nr, r_beg + q);
-  int c0 = 0;
-  for (int r = r_beg; r < r_end; ++r) c0 += (flg[row0 + r] & LH_ROW_LEADER) != 0;
-  cnt[tid] = c0;
-  __syncthreads();
-  for (int off = 1; off < kScatBwdThreads; off <<= 1) {
-    const int v = tid >= off ? cnt[tid - off] : 0;
-    __syncthreads();
-    cnt[tid] += v;
-    __syncthreads();
-  }
-  int pos = cnt[tid] - c0;
-  for (int r = r_beg; r < r_end; ++r)
-    if (flg[row0 + r] & LH_ROW_LEADER) {
-      la[pos] = anc[row0 + r];
-      lr[pos] = (int32_t)(row0 + r);
-      ++pos;
+  // leaders of the stratum in row order, rows taken one per thread: a
+  // ballot per wavefront and the wavefronts' counts place them.  Each row's
+  // flag and anchor are read once (their loads together) and the leader bit
+  // is kept in LDS for the zero rows at the end.
+  {
+    const int lane = tid & 63, wv = tid >> 6;
+    int nl_run = 0;   // leaders of the earlier batches (the same in every thread)
+    for (int b0 = 0; b0 < nr; b0 += kScatBwdThreads) {
+      const int r = b0 + tid;
+      const bool in = r < nr;
+      const uint8_t f = in ? flg[row0 + r] : (uint8_t)0;
+      const int32_t an = in ? anc[row0 + r] : 0;
+      const bool isl = (f & LH_ROW_LEADER) != 0;
+      if (in) lead[r] = isl ? 1 : 0;
+      const uint64_t bal = __ballot(isl);
+      if (lane == 0) wtot[wv] = __popcll(bal);
+      __syncthreads();
+      int before = nl_run, tot = 0;
+#pragma unroll
+      for (int i = 0; i < kScatBwdThreads / 64; ++i) {
+        before += i < wv ? wtot[i] : 0;
+        tot += wtot[i];
+      }
+      if (isl) {
+        const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
+        la[pos] = an;
+        lr[pos] = (int32_t)(row0 + r);
+      }
+      nl_run += tot;
+      __syncthreads();   // wtot is rewritten by the next batch
     }
-  if (tid == kScatBwdThreads - 1) sm.nl = cnt[tid];
+    if (tid == 0) sm.nl = nl_run;
+  }
   if (tid < G) {
     sm.tag[0][tid] = sm.tag[1][tid] = -1;
     sm.span[tid] = 0;
@@ -435,7 +447,7 @@ __global__ __launch_bounds__(kScatBwdThreads) void scatter_bwd_kernel(ScatBwdArg
   // rows that are not leaders: zeros
   const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int r = g; r < nr; r += G) {
-    if (flg[row0 + r] & LH_ROW_LEADER) continue;
+    if (lead[r]) continue;
     const int64_t row = (bh * a.S + row0 + r) * d + c * 8;
     if (a.dos) store8(a.dos + row, zero);
     if (a.dos_hi) {
@@ -448,7 +460,8 @@ __global__ __launch_bounds__(kScatBwdThreads) void scatter_bwd_kernel(ScatBwdArg
 
 static size_t scatter_bwd_lds(const Geo &g) {
   const size_t fixed = g.d == 128 ? sizeof(ScatBwdSmem<16>) : sizeof(ScatBwdSmem<8>);
-  return fixed + (2 * (size_t)(g.k_s + 1) + kScatBwdThreads) * sizeof(int32_t);
+  const size_t nr = (size_t)(g.k_s + 1);
+  return fixed + (2 * nr + kScatBwdThreads / 64) * sizeof(int32_t) + nr;   // + leader bytes
 }
 
 lh_status launch_scatter_bwd(const Geo &g, const void *dout, const int32_t *sel_anchor,
