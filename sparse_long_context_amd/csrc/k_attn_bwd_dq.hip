@@ -362,8 +362,8 @@ void attn_bwd_dq_kernel(
       x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
       x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
     };
-    unpool_strata<TO, D / 8, kQThreads>(ua, ro, ld, (TO *)ua.dx[0] + (bh * ua.N + m0 * ua.Bc) * D,
-                                        spw, tid);
+    unpool_strata<TO, D / 8, kQThreads, false>(
+        ua, ro, ld, (TO *)ua.dx[0] + (bh * ua.N + m0 * ua.Bc) * D, spw, tid);
   }
 }
 

@@ -748,10 +748,17 @@ __global__ __launch_bounds__(kUnpoolThreads) void unpool_kernel(UnpoolArgs a) {
   const int tid = threadIdx.x;
   unpool_stage_ro<kUnpoolThreads>(a, ro, a.row_of + bh * a.E, m0, a.spw, 0, a.S, tid);
   __syncthreads();
-  const float *dxs = a.dxs[z] + bh * a.S * a.d + (tid % CPR) * 8;
-  auto rows = [&](int32_t r, float *x) { load8(dxs + (int64_t)r * a.d, x); };
-  unpool_strata<TO, CPR, kUnpoolThreads>(a, ro, rows, (TO *)a.dx[z] + (bh * a.N + m0 * a.Bc) * a.d,
-                                         a.spw, tid);
+  const float *dxs = a.dxs[z] + bh * a.S * a.d + (tid % CPR) * 4;
+  const int half = a.d / 2;
+  auto rows = [&](int32_t r, float *x) {   // columns c*4 .. +3 and d/2 + c*4 .. +3
+    const float *p = dxs + (int64_t)r * a.d;
+    const float4 u = *reinterpret_cast<const float4 *>(p);
+    const float4 v = *reinterpret_cast<const float4 *>(p + half);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+  };
+  unpool_strata<TO, CPR, kUnpoolThreads, true>(
+      a, ro, rows, (TO *)a.dx[z] + (bh * a.N + m0 * a.Bc) * a.d, a.spw, tid);
 }
 
 static int unpool_spw(const Geo &g) {

@@ -102,6 +102,10 @@ typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store16_nt(void *p, uint4 v) {
   __builtin_nontemporal_store(nt_u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u32x4 *>(p));
 }
+typedef unsigned int nt_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store8b_nt(void *p, uint2 v) {
+  __builtin_nontemporal_store(nt_u32x2{v.x, v.y}, reinterpret_cast<nt_u32x2 *>(p));
+}
 __device__ __forceinline__ void store8_nt(float *p, const float *x) {
   store16_nt(p, make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
                            __float_as_uint(x[3])));

@@ -49,6 +49,11 @@ template <> struct Pack8<bf16_t> {
                    pack2_bf16(x[6], x[7]));
   }
   __device__ void put(bf16_t *p) const { store16_nt(p, w); }   // gradients: streamed out
+  // columns 0-3 at p, 4-7 at p + half
+  __device__ void put(bf16_t *p, int half) const {
+    store8b_nt(p, make_uint2(w.x, w.y));
+    store8b_nt(p + half, make_uint2(w.z, w.w));
+  }
 };
 template <> struct Pack8<float> {
   float4 a, b;
@@ -61,6 +66,12 @@ template <> struct Pack8<float> {
                              __float_as_uint(a.w)));
     store16_nt(p + 4, make_uint4(__float_as_uint(b.x), __float_as_uint(b.y),
                                  __float_as_uint(b.z), __float_as_uint(b.w)));
+  }
+  __device__ void put(float *p, int half) const {
+    store16_nt(p, make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
+                             __float_as_uint(a.w)));
+    store16_nt(p + half, make_uint4(__float_as_uint(b.x), __float_as_uint(b.y),
+                                    __float_as_uint(b.z), __float_as_uint(b.w)));
   }
 };
 
@@ -83,13 +94,22 @@ __device__ __forceinline__ void unpool_stage_ro(const UnpoolArgs &a, int32_t *ro
 // The tokens of the spw staged strata: out points at the first token row of
 // stratum m0 ([*, d], output type), rows(r, x) loads this lane's 8 columns of
 // subsequence row r (any r that ro holds).  NTHR threads, CPR lanes per row.
-template <typename TO, int CPR, int NTHR, typename Rows>
+// SPLIT: the lane's 8 columns are 4 at c*4 and 4 at d/2 + c*4 instead of 8
+// at c*8 (rows must load them in that order), and they are stored the same
+// way: every 16-byte-per-lane load of a float32 row by a lane group then
+// covers whole 128-byte lines (with 8 contiguous columns per lane each load
+// instruction covers half of every line of the row).
+template <typename TO, int CPR, int NTHR, bool SPLIT, typename Rows>
 __device__ __forceinline__ void unpool_strata(const UnpoolArgs &a, const int32_t *ro, Rows rows,
                                               TO *out, int spw, int tid) {
   const int c = tid % CPR;
   constexpr int LANES = NTHR / CPR;   // lanes along the tokens
   const int d = a.d;
-  out += c * 8;
+  out += SPLIT ? c * 4 : c * 8;
+  auto put = [&](const Pack8<TO> &v, TO *dst) {
+    if constexpr (SPLIT) v.put(dst, d / 2);
+    else v.put(dst);
+  };
   const int ntok = spw * (int)a.Bc;
   const int P1 = a.L >= 2 ? a.p : 1;    // tokens per level-1 entry
   const int nent = ntok / P1;
@@ -151,9 +171,9 @@ __device__ __forceinline__ void unpool_strata(const UnpoolArgs &a, const int32_t
           for (int i = 0; i < 8; ++i) o[i] = A[i] + x[k][i];
           Pack8<TO> v;
           v.set(o);
-          v.put(dst);
+          put(v, dst);
         } else {
-          shared_row.put(dst);
+          put(shared_row, dst);
         }
       }
     }
