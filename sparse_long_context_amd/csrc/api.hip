@@ -550,7 +550,7 @@ lh_status lh_scatter_bwd(const lh_dims *dims, const void *dout, const int32_t *s
   LH_REQ(aligned16(dout) && aligned16(dos) && aligned4(sel_anchor));
   clear_pending_error();
   return launch_scatter_bwd(g, dout, sel_anchor, sel_flags, dos, nullptr, nullptr, nullptr,
-                            nullptr, (hipStream_t)stream);
+                            nullptr, nullptr, (hipStream_t)stream);
 }
 
 lh_status lh_span_owner(const lh_dims *dims, const int32_t *row_of, int32_t *owner,
@@ -720,7 +720,9 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
     LH_TRY(launch_copy_rows(g, dout, dop, g.Nreal, g.N, (int64_t)g.d * el_size(g.out), st));
     dout = dop;
   }
-  // scatter adjoint in the layer's mode (dos float32 and/or its bf16 split)
+  // scatter adjoint in the layer's mode (dos float32 and/or its bf16 split);
+  // the hold adjoint keeps float32 dOS rows for drow in dqs, which nothing
+  // uses before the dQ kernel
   auto scatter_adj = [&](float *dos, bf16_t *hi, bf16_t *lo) -> lh_status {
     if (g.mode == LH_SCATTER_SPAN) {
       LH_TRY(launch_owner(g, s->row_of, owner, st));
@@ -728,7 +730,7 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
                                      (const float *)s->os, drow, st);
     }
     return launch_scatter_bwd(g, dout, s->sel_anchor, s->sel_flags, dos, hi, lo,
-                              (const float *)s->os, drow, st);
+                              (const float *)s->os, drow, dqs, st);
   };
   if (g.io == LH_BF16) {
     bf16_t *dhi = (bf16_t *)c.take(rows_bf16(g));

@@ -259,6 +259,7 @@ struct ScatBwdArgs {
   bf16_t *dos_hi, *dos_lo;
   const float *os;
   float *drow;
+  float *dsum;   // float32 dOS rows kept for drow (dos itself, or scratch rows)
   int64_t N, S, n_c, k_s;
   int32_t d;
 };
@@ -350,21 +351,15 @@ __global__ __launch_bounds__(kScatBwdThreads) void scatter_bwd_kernel(ScatBwdArg
 
   const int g = tid / CPR, c = tid % CPR;
   const T *dO = (const T *)a.dout + bh * a.N * d + c * 8;
-  // final value of leader k: dOS (and its split), drow = <dOS, OS>
+  // final value of leader k: dOS (and its split); its float32 row is kept
+  // for drow = <dOS, OS>, which the last phase forms for all leaders at once
+  // (a load of OS here, waited for at once, would leave the wavefront with
+  // no loads in flight at every segment's end)
   auto finish = [&](int k, const float *acc) {
     const int64_t row = (bh * a.S + lr[k]) * d + c * 8;
     if (a.dos) store8(a.dos + row, acc);
     if (a.dos_hi) store8_split(a.dos_hi + row, a.dos_lo + row, acc);
-    if (a.drow) {
-      float o[8];
-      load8(a.os + row, o);
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s += acc[i] * o[i];
-#pragma unroll
-      for (int off = 1; off < CPR; off <<= 1) s += __shfl_xor(s, off);
-      if (c == 0) a.drow[bh * a.S + lr[k]] = s;
-    }
+    if (a.drow && a.dsum != a.dos) store8(a.dsum + row, acc);
   };
 
   const int64_t n = nl > 0 ? T1 - T0 : 0;   // a valid selection has a leader per stratum
@@ -444,6 +439,37 @@ __global__ __launch_bounds__(kScatBwdThreads) void scatter_bwd_kernel(ScatBwdArg
     }
     finish(k, acc);
   }
+  // drow of every leader: its float32 dOS row (stored above by this
+  // workgroup) and its OS row, up to 4 leaders per group in flight
+  if (a.drow) {
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    constexpr int B = 4;
+    for (int k0 = g; k0 < nl; k0 += B * G) {
+      float xs[B][8], o[B][8];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int k = k0 + b * G;
+        if (k < nl) {
+          const int64_t row = (bh * a.S + lr[k]) * d + c * 8;
+          load8(a.dsum + row, xs[b]);
+          load8(a.os + row, o[b]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int k = k0 + b * G;
+        if (k < nl) {
+          float s = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s += xs[b][i] * o[b][i];
+#pragma unroll
+          for (int off = 1; off < CPR; off <<= 1) s += __shfl_xor(s, off);
+          if (c == 0) a.drow[bh * a.S + lr[k]] = s;
+        }
+      }
+    }
+  }
   // rows that are not leaders: zeros
   const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int r = g; r < nr; r += G) {
@@ -466,11 +492,14 @@ static size_t scatter_bwd_lds(const Geo &g) {
 
 lh_status launch_scatter_bwd(const Geo &g, const void *dout, const int32_t *sel_anchor,
                              const uint8_t *sel_flags, float *dos, bf16_t *dos_hi,
-                             bf16_t *dos_lo, const float *os, float *drow, hipStream_t st) {
+                             bf16_t *dos_lo, const float *os, float *drow, float *scratch,
+                             hipStream_t st) {
   ScatBwdArgs a;
   a.dout = dout; a.anchor = sel_anchor; a.flags = sel_flags; a.dos = dos;
   a.dos_hi = dos_lo ? dos_hi : nullptr; a.dos_lo = dos_lo;
   a.os = os; a.drow = os ? drow : nullptr; a.N = g.N; a.S = g.S; a.n_c = g.n_c; a.k_s = g.k_s;
+  a.dsum = dos ? dos : scratch;
+  if (a.drow && !a.dsum) return LH_ERR_INVALID_ARG;
   a.d = g.d;
   const size_t shm = scatter_bwd_lds(g);
   if (shm > kMaxLdsRows) return LH_ERR_UNSUPPORTED;

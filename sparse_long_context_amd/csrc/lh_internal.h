@@ -165,10 +165,13 @@ lh_status launch_scatter(const Geo &g, const float *os, const int32_t *sel_ancho
                          const uint8_t *sel_flags, void *o, hipStream_t st);
 // Scatter adjoint.  dos (float32) may be NULL; dos_hi/dos_lo (bf16, may be
 // NULL) receive the two-term split dos ~= hi + lo; drow[j] = <dos_j, os_j>
-// when os (float32) and drow are not NULL.  dout has the output type.
+// when os (float32) and drow are not NULL, which needs float32 rows [B*H, S,
+// d] to keep dos in: dos itself, else `scratch` (overwritten).  dout has the
+// output type.
 lh_status launch_scatter_bwd(const Geo &g, const void *dout, const int32_t *sel_anchor,
                              const uint8_t *sel_flags, float *dos, bf16_t *dos_hi,
-                             bf16_t *dos_lo, const float *os, float *drow, hipStream_t st);
+                             bf16_t *dos_lo, const float *os, float *drow, float *scratch,
+                             hipStream_t st);
 // span broadcast: owner[BH, N] int32 (finest selected entry per token), the
 // copy O[t] = OS[owner[t]], and its adjoint (outputs as launch_scatter_bwd)
 lh_status launch_owner(const Geo &g, const int32_t *row_of, int32_t *owner, hipStream_t st);
