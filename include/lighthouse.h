@@ -32,11 +32,11 @@
  *    T = (p^L - 1)/(p - 1) entries per stratum, k_s = K / n_c ranked entries
  *    per stratum, S = K + n_c subsequence rows.
  *  - Streams: all work is ordered on `stream` (a hipStream_t; NULL is the
- *    null stream) and is asynchronous.  The two layer calls also run some
- *    independent kernels on a second stream of the device that the library
- *    keeps (default priority), forked from `stream` and joined back to it by
- *    events, so that they are complete whenever `stream`'s work is.  No call
- *    synchronises or reads device memory back to the host.
+ *    null stream) and is asynchronous.  The layer backward also runs the
+ *    pooling adjoint of dK and dV on a second stream of the device that the
+ *    library keeps (default priority), forked from `stream` and joined back
+ *    to it by events, so that it is complete whenever `stream`'s work is.
+ *    No call synchronises or reads device memory back to the host.
  *  - Outputs are overwritten, never accumulated.  Token-length outputs that
  *    no later kernel of the layer reads (the layer output, the input
  *    gradients, the scatter stages' outputs) are written with nontemporal

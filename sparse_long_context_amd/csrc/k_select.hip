@@ -34,6 +34,7 @@ namespace lh {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelMaxT = 7936;     // LDS holds 8 bytes per subtree entry
+constexpr int kSelLoads = 8;       // score loads a thread keeps in flight
 
 struct SelArgs {
   const float *sq, *sk;
@@ -45,6 +46,7 @@ struct SelArgs {
   int64_t lsize[kMaxLevels], loff[kMaxLevels], pw[kMaxLevels + 1];
   int32_t cstart[kMaxLevels + 1];   // first candidate index of each level
   int32_t tsub[kMaxLevels];         // subtree size of a level-l entry
+  int32_t lgp;                      // log2(p) when p is a power of two, else -1
 };
 
 // block-wide exclusive scan of one int per thread; returns the total too
@@ -74,6 +76,12 @@ __device__ __forceinline__ int level_of_cand(const SelArgs &a, int ci) {
   return l;
 }
 
+// flat index of entry j of level l in stratum m (a level-l stratum holds
+// cstart[l+1] - cstart[l] entries)
+__device__ __forceinline__ int64_t entry_of(const SelArgs &a, int64_t m, int l, int j) {
+  return a.loff[l] + m * (int64_t)(a.cstart[l + 1] - a.cstart[l]) + j;
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
   extern __shared__ uint32_t sm[];
   const int T = a.T;
@@ -92,23 +100,50 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
   const int ncand = T - 1;
   const int64_t k_s = a.k_s;
 
-  // 1. keys and post-order map
-  for (int ci = tid; ci < T; ci += kSelThreads) {
-    const int l = level_of_cand(a, ci);
-    const int j = ci - a.cstart[l];
-    const int64_t f = a.loff[l] + m * (a.Bc / a.pw[l]) + j;
-    const float sg = a.sigma == LH_SIGMA_SUM   ? __fadd_rn(sq[f], sk[f])
-                     : a.sigma == LH_SIGMA_MAX ? fmaxf(sq[f], sk[f])
-                                               : __fmul_rn(sq[f], sk[f]);
-    key[ci] = __float_as_uint(sg);
-    st[ci] = 0;
-    int post = a.tsub[l] - 1;
-    int64_t jj = j;
-    for (int lam = l; lam <= a.L - 2; ++lam) {
-      post += (int)(jj % a.p) * a.tsub[lam];
-      jj /= a.p;
+  // 1. keys and post-order map.  A thread's score loads are all issued
+  // before any is used (one memory round trip per kSelLoads candidates),
+  // and index math stays in 32 bits (j < entries per stratum).
+  for (int c0 = 0; c0 < T; c0 += kSelThreads * kSelLoads) {
+    float s1[kSelLoads], s2[kSelLoads];
+#pragma unroll
+    for (int u = 0; u < kSelLoads; ++u) {
+      const int ci = c0 + u * kSelThreads + tid;
+      s1[u] = s2[u] = 0.f;
+      if (ci < T) {
+        const int l = level_of_cand(a, ci);
+        const int64_t f = entry_of(a, m, l, ci - a.cstart[l]);
+        s1[u] = sq[f];
+        s2[u] = sk[f];
+      }
     }
-    post2c[post] = (uint16_t)ci;
+#pragma unroll
+    for (int u = 0; u < kSelLoads; ++u) {
+      const int ci = c0 + u * kSelThreads + tid;
+      if (ci >= T) break;
+      const int l = level_of_cand(a, ci);
+      const float sg = a.sigma == LH_SIGMA_SUM   ? __fadd_rn(s1[u], s2[u])
+                       : a.sigma == LH_SIGMA_MAX ? fmaxf(s1[u], s2[u])
+                                                 : __fmul_rn(s1[u], s2[u]);
+      key[ci] = __float_as_uint(sg);
+      st[ci] = 0;
+      // post-order position: the subtree of each ancestor's earlier
+      // siblings precedes this entry
+      int post = a.tsub[l] - 1;
+      int jj = ci - a.cstart[l];
+      for (int lam = l; lam <= a.L - 2; ++lam) {
+        int q, r;
+        if (a.lgp >= 0) {
+          q = jj >> a.lgp;
+          r = jj - (q << a.lgp);
+        } else {
+          q = jj / a.p;
+          r = jj - q * a.p;
+        }
+        post += r * a.tsub[lam];
+        jj = q;
+      }
+      post2c[post] = (uint16_t)ci;
+    }
   }
   __syncthreads();
 
@@ -197,7 +232,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
     const int ci = post2c[q];
     const int l = level_of_cand(a, ci);
     const int j = ci - a.cstart[l];
-    const int64_t f = a.loff[l] + m * (a.Bc / a.pw[l]) + j;
+    const int64_t f = entry_of(a, m, l, j);
     if ((st[ci] & 1) && r <= k_s) {
       const int64_t anchor = m * a.Bc + (int64_t)(j + 1) * a.pw[l] - 1;
       sel_idx[row0 + r] = (int32_t)f;
@@ -243,6 +278,9 @@ lh_status launch_select(const Geo &g, const float *sq, const float *sk, int32_t 
     a.tsub[l] = (int32_t)((g.pw[l + 1] - 1) / (g.p - 1));
   }
   a.cstart[g.L] = cs;
+  a.lgp = -1;
+  for (int k = 0; k < 31; ++k)
+    if ((1 << k) == g.p) a.lgp = k;
   const size_t shm = (size_t)g.T * 8;
   dim3 grid((unsigned)g.n_c, (unsigned)g.BH());
   hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), shm, st, a);
