@@ -736,9 +736,10 @@ lh_status lh_layer_bwd(const lh_dims *dims, const lh_saved *s, const void *dout,
     void *out_kv[2] = {grad[1], grad[2]};
     LH_TRY(launch_unpool(g, in_kv, s->row_of, out_kv, 2, side));
     if (dq_can_unpool(g)) {
-      // every dQ workgroup's 128 rows are whole strata: it runs the gather +
-      // pooling adjoint of its own rows in its epilogue (no dQS round trip,
-      // and dQ's token writes overlap other workgroups' MFMA work)
+      // d = 64 and every dQ workgroup's 128 rows are whole strata: it runs
+      // the gather + pooling adjoint of its own rows in its epilogue (no dQS
+      // round trip, and dQ's token writes overlap the MFMA work of the other
+      // workgroup on its CU); otherwise dQS, then dQ's own unpool launch
       LH_TRY(launch_attn_bwd_dq_unpool(g, (const bf16_t *)s->qs, (const bf16_t *)s->ks,
                                        (const bf16_t *)s->vs, dhi, dlo, s->lse, drow,
                                        s->sel_flags, s->row_of, grad[0], st));

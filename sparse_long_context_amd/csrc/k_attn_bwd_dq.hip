@@ -390,14 +390,16 @@ lh_status check_attn_dq_supported(const Geo &g) {
   return dq_lds(g, false) <= kMaxLds ? LH_OK : LH_ERR_UNSUPPORTED;
 }
 
-// whether the dQ kernel can run the pooling adjoint of its own rows: every
-// workgroup's 128 rows are whole strata, and the epilogue's LDS stays within
-// the budget that keeps the kernel's occupancy (two workgroups per CU at
-// d = 64)
+// whether the dQ kernel runs the pooling adjoint of its own rows: d = 64
+// (two workgroups per CU, so one's epilogue writes overlap the other's MFMA
+// work; at d = 128 a workgroup holds its CU alone, and a separate unpool
+// launch after the kernel was measured faster on both d = 128 workloads),
+// every workgroup's 128 rows are whole strata, and the epilogue's LDS stays
+// within the budget that keeps two workgroups per CU
 bool dq_can_unpool(const Geo &g) {
+  if (g.d != 64) return false;
   if (g.io != LH_BF16 || kQBQ % (g.k_s + 1) != 0 || g.T > kUnpoolLdsEntries) return false;
-  const size_t cap = g.d == 64 ? kMaxLds / 2 : kMaxLds;
-  return dq_lds(g, true) <= cap && dq_lds(g, false) <= cap;
+  return dq_lds(g, true) <= kMaxLds / 2 && dq_lds(g, false) <= kMaxLds / 2;
 }
 
 static lh_status launch_dq(const Geo &g, const bf16_t *qs, const bf16_t *ks, const bf16_t *vs,
@@ -423,7 +425,7 @@ static lh_status launch_dq(const Geo &g, const bf16_t *qs, const bf16_t *ks, con
                        g.scale, ua, rps);                                                     \
   } while (0)
   if (g.d == 128) {
-    if (epi == 0) LH_DQ(128, 0); else if (epi == 1) LH_DQ(128, 1); else LH_DQ(128, 2);
+    LH_DQ(128, 0);   // the epilogue forms run at d = 64 only (dq_can_unpool)
   } else {
     if (epi == 0) LH_DQ(64, 0); else if (epi == 1) LH_DQ(64, 1); else LH_DQ(64, 2);
   }

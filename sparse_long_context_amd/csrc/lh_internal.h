@@ -215,8 +215,9 @@ lh_status launch_attn_bwd_dq_bf16(const Geo &g, const bf16_t *qs, const bf16_t *
                                   float *dqs, hipStream_t st);
 // The same dQ kernel with the gather + pooling adjoint of its own rows in
 // the epilogue (the layer backward): dq [BH, N, d] of the output type
-// instead of the float32 subsequence rows.  Only where every workgroup's
-// 128 rows are whole strata and the epilogue's LDS fits (dq_can_unpool).
+// instead of the float32 subsequence rows.  Only at d = 64, where every
+// workgroup's 128 rows are whole strata and the epilogue's LDS fits
+// (dq_can_unpool).
 bool dq_can_unpool(const Geo &g);
 lh_status launch_attn_bwd_dq_unpool(const Geo &g, const bf16_t *qs, const bf16_t *ks,
                                     const bf16_t *vs, const bf16_t *dos_hi,
