@@ -52,9 +52,9 @@
  *    stream (below) the join back to `stream` is made on every return path,
  *    error paths included.  No C++ exception crosses the ABI.
  *  - Concurrency: calls are reentrant; the library has no mutable global
- *    state apart from a per-device property cache and a per-device second
- *    stream with three events, each created once under a lock and kept until
- *    the process ends.
+ *    state apart from a per-device second stream with two events and the
+ *    per-device address of the no-alloc entry point's scratch array, each
+ *    set once under a lock and kept until the process ends.
  *  - Determinism: every kernel is free of atomics on floating-point data;
  *    results are bitwise reproducible run to run.
  */
