@@ -773,7 +773,8 @@ __global__ __launch_bounds__(kUnpoolThreads) void unpool_kernel(UnpoolArgs a) {
   extern __shared__ int32_t ro[];
   const int z = blockIdx.z;
   const int64_t bh = blockIdx.y;
-  const int64_t m0 = (int64_t)blockIdx.x * a.spw;   // first stratum of the workgroup
+  const int part = (int)(blockIdx.x % (unsigned)a.parts);
+  const int64_t m0 = (int64_t)(blockIdx.x / (unsigned)a.parts) * a.spw;   // first stratum
   const int tid = threadIdx.x;
   unpool_stage_ro<kUnpoolThreads>(a, ro, a.row_of + bh * a.E, m0, a.spw, 0, a.S, tid);
   __syncthreads();
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(kUnpoolThreads) void unpool_kernel(UnpoolArgs a) {
     x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
   };
   unpool_strata<TO, CPR, kUnpoolThreads, true>(
-      a, ro, rows, (TO *)a.dx[z] + (bh * a.N + m0 * a.Bc) * a.d, a.spw, tid);
+      a, ro, rows, (TO *)a.dx[z] + (bh * a.N + m0 * a.Bc) * a.d, a.spw, tid, part, a.parts);
 }
 
 static int unpool_spw(const Geo &g) {
@@ -814,7 +815,7 @@ lh_status check_rows_supported(const Geo &g) {
                   grid_fits(cdiv(N, 256), 256) &&                   // owner
                   grid_fits(cdiv(N, (256 / cpr) * 8), 256) &&       // span scatter
                   grid_fits(cdiv(BH * S, 4), 256) &&                // dos_prep (all heads)
-                  grid_fits(g.n_c, kUnpoolThreads);                  // unpool
+                  grid_fits(2 * g.n_c, kUnpoolThreads);              // unpool (up to 2 parts)
   if (!ok) return LH_ERR_UNSUPPORTED;
   return g.T <= kUnpoolLdsEntries ? LH_OK : LH_ERR_UNSUPPORTED;
 }
@@ -828,6 +829,7 @@ UnpoolArgs make_unpool_args(const Geo &g, int spw) {
   a.row_of = nullptr;
   a.N = g.N; a.E = g.E; a.S = g.S; a.Bc = g.Bc; a.d = g.d; a.L = g.L; a.p = g.p;
   a.spw = spw;
+  a.parts = 1;
   a.lgp = -1;
   for (int k = 0; k < 31; ++k)
     if ((1 << k) == g.p) a.lgp = k;
@@ -853,8 +855,12 @@ lh_status launch_unpool(const Geo &g, const float *const dxs[], const int32_t *r
     a.dx[i] = dx[i];
   }
   a.row_of = row_of;
+  // one tensor alone (the layer's dQ at d = 128, after the dQ kernel): two
+  // workgroups per group of strata, so the launch keeps as many loads in
+  // flight as the three-tensor one
+  a.parts = nt == 1 ? 2 : 1;
   const size_t smem = (size_t)a.spw * g.T * sizeof(int32_t);
-  dim3 grid((unsigned)(g.n_c / a.spw), (unsigned)g.BH(), (unsigned)nt);
+  dim3 grid((unsigned)(g.n_c / a.spw * a.parts), (unsigned)g.BH(), (unsigned)nt);
   if (g.out == LH_BF16) {
     if (g.d == 128) hipLaunchKernelGGL((unpool_kernel<bf16_t, 16>), grid, dim3(kUnpoolThreads), smem, st, a);
     else hipLaunchKernelGGL((unpool_kernel<bf16_t, 8>), grid, dim3(kUnpoolThreads), smem, st, a);

@@ -30,6 +30,7 @@ struct UnpoolArgs {
   const int32_t *row_of;
   int64_t N, E, S, Bc;
   int32_t d, L, p, spw, lgp;    // lgp = log2(p) when p is a power of two, else -1
+  int32_t parts;                // workgroups per group of spw strata (each a run of entries)
   int64_t loff[kMaxLevels];
   int32_t per[kMaxLevels];      // entries of level l per stratum (Bc / p^l)
   int32_t pw[kMaxLevels];       // p^l
@@ -99,9 +100,12 @@ __device__ __forceinline__ void unpool_stage_ro(const UnpoolArgs &a, int32_t *ro
 // way: every 16-byte-per-lane load of a float32 row by a lane group then
 // covers whole 128-byte lines (with 8 contiguous columns per lane each load
 // instruction covers half of every line of the row).
+// part, parts: this workgroup takes the part-th of `parts` equal runs of the
+// strata's level-1 entries (whole strata: part 0 of 1).
 template <typename TO, int CPR, int NTHR, bool SPLIT, typename Rows>
 __device__ __forceinline__ void unpool_strata(const UnpoolArgs &a, const int32_t *ro, Rows rows,
-                                              TO *out, int spw, int tid) {
+                                              TO *out, int spw, int tid, int part = 0,
+                                              int parts = 1) {
   const int c = tid % CPR;
   constexpr int LANES = NTHR / CPR;   // lanes along the tokens
   const int d = a.d;
@@ -112,9 +116,11 @@ __device__ __forceinline__ void unpool_strata(const UnpoolArgs &a, const int32_t
   };
   const int ntok = spw * (int)a.Bc;
   const int P1 = a.L >= 2 ? a.p : 1;    // tokens per level-1 entry
-  const int nent = ntok / P1;
-  const int span = (nent + LANES - 1) / LANES;
-  const int e_begin = (tid / CPR) * span, e_end = min(nent, e_begin + span);
+  const int nall = ntok / P1;
+  const int per_part = (nall + parts - 1) / parts;
+  const int p_begin = part * per_part, nent = min(nall, p_begin + per_part);
+  const int span = (nent - p_begin + LANES - 1) / LANES;
+  const int e_begin = p_begin + (tid / CPR) * span, e_end = min(nent, e_begin + span);
   auto anc = [&](int u, int l) { return a.lgp >= 0 ? (u >> (a.lgp * l)) : u / a.pw[l]; };
   float A2[8];
 #pragma unroll
