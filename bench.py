@@ -15,8 +15,11 @@ run as the one-level layer), and the CPU oracle timed on a bounded sample of
 the same workload.
 
 The step time is the median of the K timed steps (events between
-consecutive steps).  With the default (128K-token) workload the line also
-carries the step times of the other three large workloads ("workloads").
+consecutive steps).  With the stages on, the layer is timed again after
+them ("mode_orders": the two orders of layer and stage mode); the headline
+is the first measurement.  With the default (128K-token) workload the line
+also carries the step times of the other three large workloads
+("workloads").
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 4]
                        [--no-cpu] [--no-stages] [--no-dense] [--no-workloads]
@@ -479,6 +482,18 @@ def main():
         for n, e in stages.items():
             print(f"[bench] stage {n:20s} {e}", file=sys.stderr, flush=True)
 
+    # the layer timed again after the stages (the opposite order of the two
+    # modes); the headline stays the first, layer-first, measurement
+    orders = None
+    if stages is not None:
+        ms2, _ = time_steps(torch, step, args.warmup, args.steps)
+        orders = {"layer_first_ms": round(ms, 4), "stages_first_ms": round(ms2, 4),
+                  "median_of_the_two_ms": round(float(np.median([ms, ms2])), 4),
+                  "how": "median step of the layer timed before the per-stage runs and again "
+                         "after them"}
+        print(f"[bench] layer fwd+bwd after the stages {ms2:.3f} ms/step", file=sys.stderr,
+              flush=True)
+
     dense = dense_mine = None
     if not args.no_dense and w.dtype == "bf16":
         best = dense_sdpa(torch, Q, K, V, dO)
@@ -528,7 +543,8 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "N": w.N, "H": w.H, "d": w.d, "p": w.p,
                    "L": w.L, "S": S, "K": w.K, "io_dtype": w.dtype, "out_dtype": w.dtype},
         "roofline": roof, "cpu_baseline": cpu, "measured_peaks": peaks, "cold": cold, "dense_sdpa": dense,
-        "dense_own_kernels": dense_mine, "stages": stages, "workloads": others,
+        "dense_own_kernels": dense_mine, "stages": stages, "mode_orders": orders,
+        "workloads": others,
     }
     print(json.dumps(line))
 
