@@ -15,9 +15,9 @@ run as the one-level layer), and the CPU oracle timed on a bounded sample of
 the same workload.
 
 The step time is the median of the K timed steps (events between
-consecutive steps).  With the stages on, the layer is timed again after
-them ("mode_orders": the two orders of layer and stage mode); the headline
-is the first measurement.  With the default (128K-token) workload the line
+consecutive steps).  With the stages on, the layer is timed before them and
+again after them ("mode_orders": the two orders of layer and stage mode);
+the headline is the second, taken with the GPU at its steady clock.  With the default (128K-token) workload the line
 also carries the step times of the other three large workloads
 ("workloads").
 
@@ -369,10 +369,17 @@ def main():
               f"{args.copy_mib} MiB)", file=sys.stderr, flush=True)
         del src, dst
 
-    ms, ms_mean = time_steps(torch, step, args.warmup, args.steps)
-    value = w.B * w.N / (ms / 1e3)
-    print(f"[bench] layer fwd+bwd {ms:.3f} ms/step (median; mean {ms_mean:.3f})",
-          file=sys.stderr, flush=True)
+    peaks = measured_peaks(torch, dev)
+    print(f"[bench] measured ceilings {peaks}", file=sys.stderr, flush=True)
+
+    # The layer is timed twice, before the per-stage runs and after them
+    # (the two orders of layer and stage mode).  The headline is the second:
+    # timed right after the W warm-up steps of a cold start the GPU has not
+    # reached its steady clock (at 128K, 1.558-1.577 ms with 5 warm-up steps
+    # against 1.516 ms with 50, and 1.520-1.523 ms after the stage runs).
+    ms_first, ms_first_mean = time_steps(torch, step, args.warmup, args.steps)
+    print(f"[bench] layer fwd+bwd {ms_first:.3f} ms/step (median; mean {ms_first_mean:.3f}), "
+          "before the stages", file=sys.stderr, flush=True)
 
     # cold caches: before each rep a 1 GiB read evicts the L2 and the 256 MB
     # Infinity Cache, leaving them holding clean lines of another buffer (a
@@ -404,9 +411,6 @@ def main():
                 "how": "each step timed alone after a 1 GiB device read that evicts the L2 and the "
                        "Infinity Cache; the headline value is the back-to-back (warm) rate"}
         print(f"[bench] layer fwd+bwd cold {cms:.3f} ms/step", file=sys.stderr, flush=True)
-
-    peaks = measured_peaks(torch, dev)
-    print(f"[bench] measured ceilings {peaks}", file=sys.stderr, flush=True)
 
     stages, roof = None, None
     if not args.no_stages and w.dtype == "bf16":
@@ -482,17 +486,19 @@ def main():
         for n, e in stages.items():
             print(f"[bench] stage {n:20s} {e}", file=sys.stderr, flush=True)
 
-    # the layer timed again after the stages (the opposite order of the two
-    # modes); the headline stays the first, layer-first, measurement
+    # the headline: W warm-up steps and K timed steps after the stage runs
+    # (without them, the first measurement)
     orders = None
+    ms, ms_mean = ms_first, ms_first_mean
     if stages is not None:
-        ms2, _ = time_steps(torch, step, args.warmup, args.steps)
-        orders = {"layer_first_ms": round(ms, 4), "stages_first_ms": round(ms2, 4),
-                  "median_of_the_two_ms": round(float(np.median([ms, ms2])), 4),
+        ms, ms_mean = time_steps(torch, step, args.warmup, args.steps)
+        orders = {"layer_first_ms": round(ms_first, 4), "stages_first_ms": round(ms, 4),
+                  "median_of_the_two_ms": round(float(np.median([ms_first, ms])), 4),
                   "how": "median step of the layer timed before the per-stage runs and again "
-                         "after them"}
-        print(f"[bench] layer fwd+bwd after the stages {ms2:.3f} ms/step", file=sys.stderr,
-              flush=True)
+                         "after them; the headline is the second"}
+        print(f"[bench] layer fwd+bwd {ms:.3f} ms/step (median; mean {ms_mean:.3f}), after the "
+              "stages (headline)", file=sys.stderr, flush=True)
+    value = w.B * w.N / (ms / 1e3)
 
     dense = dense_mine = None
     if not args.no_dense and w.dtype == "bf16":
