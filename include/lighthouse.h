@@ -71,7 +71,7 @@ extern "C" {
 typedef int32_t lh_status;
 #define LH_OK               0
 #define LH_ERR_INVALID_ARG (-1)   /* bad geometry, null or misaligned pointer */
-#define LH_ERR_UNSUPPORTED (-2)   /* valid geometry this build does not cover */
+#define LH_ERR_UNSUPPORTED (-2)   /* valid geometry this library does not cover */
 #define LH_ERR_WORKSPACE   (-3)   /* workspace missing or too small           */
 #define LH_ERR_HIP         (-4)   /* a HIP launch or runtime call failed      */
 
@@ -128,7 +128,7 @@ typedef void *lh_stream;     /* a hipStream_t */
  *   scatter_mode in {LH_SCATTER_HOLD, LH_SCATTER_SPAN},
  *   sigma_mode in {LH_SIGMA_SUM, LH_SIGMA_MAX, LH_SIGMA_PRODUCT},
  *   strata_mode in {LH_STRATA_JOINT, LH_STRATA_PER_LEVEL};
- * and the launch limits of this build (LH_ERR_UNSUPPORTED otherwise):
+ * and the launch limits of this library (LH_ERR_UNSUPPORTED otherwise):
  *   B*H <= 65535, S < 2^31, T <= 7936 (one stratum's subtree in LDS), a
  *   pyramid plan with B_c / p^g <= 256 / (d/8) rows for some g <= 6,
  *   every grid's work-items along x within 2^32 - 1 (e.g. 64*B*H*S),
